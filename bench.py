@@ -1,0 +1,178 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched paged MLA decode on one MI355X.
+
+One step = one mla_decode call (split-KV kernel + LSE combine) over the
+whole batch of the DeepSeek-style decode workload: 64 requests, 1 query
+token, 128 heads, 576-wide bf16 latent rows in 64-token pages, sequence
+lengths uniform in [1024, 4096], scattered block tables, N(0,1) values.
+Inputs are generated on the host once and copied to the GPU before the
+timed region.  To keep the KV pool from being served by the 256 MB
+last-level cache instead of HBM, the timed steps rotate over several
+device copies of the pool and the query (together at least --rotate-gib).
+
+Prints one JSON line (see the keys below).  --gpus above 1 is refused: the
+decode runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode KV-cache GB/s + TFLOPS (% of HBM/MFMA roofline), 128 heads bf16"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def cpu_baseline(inp, nbytes):
+    """The CPU oracle on the host cores, over the same workload (all requests, all heads)."""
+    import oracle
+    orc = oracle.default()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    t0 = time.perf_counter()
+    orc.decode(inp)
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"the whole workload once ({inp.batch} requests x {inp.q_len * inp.heads} query rows, "
+                      f"{int(inp.seq_lens.sum())} cached tokens), fp64 C oracle, OpenMP over query rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="deepseek_decode")
+    ap.add_argument("--rotate-gib", type=float, default=1.5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; the decode runs on one GPU "
+              f"(requests shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import paged_mla_decode_06_amd as mla
+    from mla_synth import generate, WORKLOADS
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    inp = generate(w)
+    kv_bytes = 1 if inp.kv_fp8 else 2
+    nbytes, flops = mla.algorithmic_work(inp.seq_lens, inp.q_len, inp.heads, inp.page_size, kv_bytes)
+
+    # device inputs, rotated over enough copies to exceed the last-level cache
+    q0 = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    if inp.kv_fp8:
+        pool0 = torch.from_numpy(inp.pool).view(torch.float8_e4m3fn).to(dev)
+    else:
+        pool0 = torch.from_numpy(inp.pool.view(np.int16)).view(torch.bfloat16).to(dev)
+    per_copy = pool0.numel() * pool0.element_size() + q0.numel() * 2
+    copies = max(2, math.ceil(args.rotate_gib * (1 << 30) / per_copy))
+    qs = [q0] + [q0.clone() for _ in range(copies - 1)]
+    pools = [pool0] + [pool0.clone() for _ in range(copies - 1)]
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    sl = torch.from_numpy(inp.seq_lens).to(dev)
+    out = torch.empty((inp.batch, inp.q_len, inp.heads, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((inp.batch, inp.q_len, inp.heads), dtype=torch.float32, device=dev)
+    p = mla.params_for(q0, pool0, bt, inp.max_seq_len, inp.softmax_scale, inp.k_scale,
+                       min_work_units=w.min_work_units)
+    ws = mla.alloc_workspace(p, dev)
+    stream = torch.cuda.current_stream()
+
+    ev = HipEvents()
+    events = [(ev.create(), ev.create(), ev.create()) for _ in range(args.steps)]
+    for i in range(args.warmup):
+        mla.mla_decode_timed(p, qs[i % copies], pools[i % copies], bt, sl, out, lse, ws, stream, None, None, None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        i = args.warmup + k
+        mla.mla_decode_timed(p, qs[i % copies], pools[i % copies], bt, sl, out, lse, ws, stream, *events[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    split_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b, _ in events]))
+    comb_ms = float(np.mean([ev.elapsed_ms(b, c) for _, b, c in events]))
+    call_ms = float(np.mean([ev.elapsed_ms(a, c) for a, _, c in events]))
+    for e in events:
+        for x in e:
+            ev.destroy(x)
+    assert torch.isfinite(out.float()).all().item(), "non-finite output"
+
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    kv_only = int(inp.seq_lens.astype(np.int64).sum()) * 576 * kv_bytes
+    split_gbs = nbytes / (split_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3fn-kv/bf16" if inp.kv_fp8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": inp.batch, "q_len": inp.q_len, "heads": inp.heads,
+                   "page_size": inp.page_size, "kv_dtype": w.kv, "seq_lens": f"{w.lens}", "seed": w.seed,
+                   "cached_tokens": int(inp.seq_lens.sum()), "num_pages": inp.num_pages,
+                   "rotating_copies": copies},
+        "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "kv_gbs": round(kv_only / (ms_step * 1e-3) / 1e9, 2),
+        "decode_tokens_per_s": round(inp.batch * inp.q_len / (ms_step * 1e-3), 1),
+        "algorithmic_bytes": nbytes,
+        "algorithmic_flops": flops,
+        "event_ms": {"split_kernel": round(split_ms, 5), "combine_kernel": round(comb_ms, 5),
+                     "call": round(call_ms, 5)},
+        "roofline": {"bound": "hbm", "achieved": round(split_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "mla_split_kernel", "mfma_frac": round(
+                         flops / (split_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, nbytes)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * libmla.h -- C ABI of libmla: batched paged Multi-head Latent Attention
+ * (MLA) decode over a compressed latent KV cache, for AMD MI355X (gfx950).
+ *
+ * The operation is the decode call of the attention backends of
+ * "sglang trtllm_mla_backend.py" (TRTLLMMLABackend._run_decode_kernel and
+ * forward_decode) and "tokenspeed flashmla.py" (FlashMLABackend.forward_decode,
+ * and forward_extend with causal=True for several query tokens):
+ *
+ *   For request b (L = seq_lens[b] cached tokens, the q_len new ones
+ *   included), query token j < q_len and head h, the visible tokens are
+ *   t < L - q_len + 1 + j (bottom-right causal alignment).  Token t's row is
+ *   pool[block_table[b][t / page_size]][t % page_size][0:576]: the 512-wide
+ *   latent c_kv followed by the 64-wide rope key.  One latent row serves all
+ *   heads (one KV head).
+ *
+ *     s_t = softmax_scale * k_scale * (q[b,j,h,0:576] . row_t)
+ *     out[b,j,h,c] = sum_t softmax(s)_t * k_scale * row_t[c],  c < 512
+ *     lse[b,j,h]   = ln sum_t exp(s_t)
+ *
+ *   k_scale applies only to an fp8 pool (the bmm1 scale rule of
+ *   _compute_decode_bmm1_scale); a bf16 pool ignores it.  A query row with no
+ *   visible token gets out = 0 and lse = -inf (the zero-KV row convention of
+ *   the sglang backend).
+ *
+ * Conventions for every entry point:
+ *  - All pointers marked "device" are HIP device pointers; the library never
+ *    allocates, frees or synchronises, and enqueues all work on `stream`
+ *    (a hipStream_t; NULL = the null stream).  The caller owns every buffer.
+ *  - Arguments are validated on the host before anything is enqueued; an
+ *    error status means nothing was enqueued.
+ *  - Device data are trusted the way the pages trust them: seq_lens[b] must
+ *    lie in [0, max_seq_len] (values outside are clamped), and every
+ *    block-table entry a request reads (index < ceil(seq_lens[b] /
+ *    page_size)) must lie in [0, num_pages).  An entry outside that range is
+ *    read as a page of zeros, never dereferenced.  Entries past a request's
+ *    last page are never read and may hold anything (-1, 0, ...).
+ *    mla_check_inputs_host() checks all of this on host copies.
+ *  - A workspace must not be shared by calls that may run concurrently.
+ */
+#ifndef LIBMLA_H
+#define LIBMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_VALUE = 1,       /* a bad argument (cf. the ValueError for page sizes other than 32/64) */
+  MLA_ERR_NOT_SUPPORTED = 2,       /* valid but unsupported (dims other than 512+64, not a gfx950 device) */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below mla_decode_workspace_size() */
+  MLA_ERR_HIP = 4                  /* a HIP runtime call or kernel launch failed */
+} mla_status;
+
+typedef enum {
+  MLA_KV_BF16 = 0,        /* pool elements are bfloat16 */
+  MLA_KV_FP8_E4M3FN = 1   /* pool elements are OCP float8_e4m3fn codes, dequantised as code * k_scale */
+} mla_kv_dtype;
+
+typedef struct {
+  int32_t batch;              /* B >= 0 requests; B = 0 enqueues nothing. At most 16384. */
+  int32_t q_len;              /* query tokens per request, 1..64 (q_len > 1: causal, bottom-right aligned) */
+  int32_t num_heads;          /* H query heads per request (this GPU's share), 1..256; q_len*H <= 4096 */
+  int32_t kv_lora_rank;       /* must be 512 (latent width = output width per head) */
+  int32_t qk_rope_head_dim;   /* must be 64 */
+  int32_t page_size;          /* tokens per page: 32 or 64 */
+  int32_t num_pages;          /* pages in the pool, >= 1 */
+  int32_t block_table_stride; /* W: int32 elements between block-table rows, >= ceil(max_seq_len/page_size) */
+  int32_t max_seq_len;        /* upper bound of seq_lens, 0 <= max_seq_len <= W*page_size */
+  int32_t kv_dtype;           /* an mla_kv_dtype */
+  float softmax_scale;        /* finite, > 0 (1/sqrt(qk_nope_head_dim + qk_rope_head_dim)) */
+  float k_scale;              /* fp8 pool: finite, > 0; bf16 pool: ignored */
+  int32_t num_splits;         /* 0: the balanced planner; n > 0: split every request's token range into
+                                 min(n, its 32-token tiles) pieces, one workgroup each (at most 1024) */
+  int32_t min_work_units;     /* balanced planner: 0 = one workgroup per compute unit; n > 0 = n workgroups */
+  int32_t num_cus;            /* 0: read the compute-unit count of the current device; n > 0: use n
+                                 (lets host-only planning calls run without a device) */
+} mla_decode_params;
+
+/* MLA_ABI_VERSION of the built library. */
+int32_t mla_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* mla_status_str(int32_t status);
+
+/* Bytes of device workspace mla_decode() needs for these parameters (split-KV
+ * partial results and planning scratch).  No device memory is touched; with
+ * num_cus == 0 and min_work_units == 0 and num_splits == 0 it queries the
+ * current device's compute-unit count.  The workspace needs no
+ * initialisation. */
+mla_status mla_decode_workspace_size(const mla_decode_params* p, size_t* bytes);
+
+/* The decode.  Layouts (all row-major, contiguous):
+ *   q           device, bf16  [B][q_len][H][576]  absorbed query: latent 512 then rope 64
+ *   kv_pool     device, bf16 or e4m3fn [num_pages][page_size][576]
+ *   block_table device, int32 [B][block_table_stride]
+ *   seq_lens    device, int32 [B]  cached tokens per request, the q_len new tokens included
+ *   out         device, bf16  [B][q_len][H][512]   (written)
+ *   lse         device, fp32  [B][q_len][H] natural-log LSE of the scaled scores, or NULL
+ *   workspace   device, >= mla_decode_workspace_size() bytes, 256-byte aligned
+ * Enqueues up to two kernels on `stream` (split-KV decode, then the LSE
+ * combine of split pieces) and returns without waiting. */
+mla_status mla_decode(const mla_decode_params* p, const void* q, const void* kv_pool, const int32_t* block_table,
+                      const int32_t* seq_lens, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* mla_decode() that also records three caller-created HIP events (hipEvent_t,
+ * each may be NULL) on `stream`: before the split-KV kernel, between it and
+ * the combine kernel, and after the combine, so that a benchmark can time the
+ * two kernels separately.  Same arguments, layouts and errors as mla_decode(). */
+mla_status mla_decode_timed(const mla_decode_params* p, const void* q, const void* kv_pool,
+                            const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_split_done,
+                            void* ev_end);
+
+/* Debug/test: copy the stored rows of request b's first min(seq_lens[b],
+ * max_seq_len) tokens, byte for byte, into dst [.. ][576] (device, pool
+ * element type) through the same page addressing the decode uses.  Rows
+ * past that count are not written. */
+mla_status mla_gather_kv(const mla_decode_params* p, const void* kv_pool, const int32_t* block_table,
+                         const int32_t* seq_lens, int32_t b, void* dst, void* stream);
+
+/* Host mirror of the work plan (CPU only, no device access when p->num_cus >
+ * 0 or p->min_work_units > 0 or p->num_splits > 0).  A plan assigns each
+ * workgroup g < grid a list of pieces (g, b, row_block, tile_begin,
+ * tile_end, slot): rows [64*row_block, 64*row_block+64) of request b's
+ * q_len*H query rows (row = j*H + h) over 32-token tiles [tile_begin,
+ * tile_end) of its tokens; slot < 0
+ * means the piece covers the whole request and writes the output directly,
+ * otherwise it writes a partial result to that workspace slot for the
+ * combine.  pieces: host, int32 [max_pieces][6].  Returns
+ * MLA_ERR_INVALID_VALUE if more than max_pieces pieces exist (*n_pieces then
+ * holds the count needed). */
+mla_status mla_plan_host(const mla_decode_params* p, const int32_t* seq_lens_host, int32_t* pieces,
+                         int32_t max_pieces, int32_t* n_pieces, int32_t* grid);
+
+/* Debug/test: the same plan computed on the device by the code the decode
+ * kernel runs.  pieces: device int32 [grid][max_per_wg][6]; counts: device
+ * int32 [grid] (pieces of each workgroup, possibly above max_per_wg, in
+ * which case only the first max_per_wg are written).  grid is what
+ * mla_plan_host() reports for the same parameters. */
+mla_status mla_plan_device(const mla_decode_params* p, const int32_t* seq_lens, int32_t* pieces,
+                           int32_t max_per_wg, int32_t* counts, int32_t grid, void* stream);
+
+/* Host-side input check (CPU only): every seq_lens[b] in [0, max_seq_len]
+ * and every block-table entry a request reads in [0, num_pages).
+ * MLA_ERR_INVALID_VALUE on the first violation. */
+mla_status mla_check_inputs_host(const mla_decode_params* p, const int32_t* block_table_host,
+                                 const int32_t* seq_lens_host);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMLA_H */

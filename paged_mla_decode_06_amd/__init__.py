@@ -1,0 +1,256 @@
+"""Python binding of libmla, the gfx950 paged MLA decode library.
+
+Argument marshalling only: every step of the decode runs in the library's
+HIP kernels; torch supplies device memory (``data_ptr()``) and the current
+stream.  The function names are those of the C ABI in ``include/libmla.h``.
+If ``libmla.so`` has not been built, every call raises ``RuntimeError``:
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "libmla.h")
+
+MLA_OK = 0
+MLA_ERR_INVALID_VALUE = 1
+MLA_ERR_NOT_SUPPORTED = 2
+MLA_ERR_WORKSPACE_TOO_SMALL = 3
+MLA_ERR_HIP = 4
+MLA_KV_BF16 = 0
+MLA_KV_FP8_E4M3FN = 1
+
+ROW_DIM = 576
+LATENT_DIM = 512
+ROPE_DIM = 64
+ROWS_PER_BLOCK = 64     # query rows per workgroup
+TILE = 32               # tokens per KV tile
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_name(status)} ({status})")
+        self.status = status
+
+
+class mla_decode_params(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "q_len", "num_heads", "kv_lora_rank", "qk_rope_head_dim", "page_size", "num_pages",
+        "block_table_stride", "max_seq_len", "kv_dtype")] + [
+        ("softmax_scale", ctypes.c_float), ("k_scale", ctypes.c_float)] + [
+        (n, ctypes.c_int32) for n in ("num_splits", "min_work_units", "num_cus")]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmla.so; raises RuntimeError if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libmla.so is not built ({LIB_PATH}); run __graft_entry__.build() or "
+                               "python -m paged_mla_decode_06_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(mla_decode_params)
+        vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+        L.mla_abi_version.restype = ctypes.c_int32
+        L.mla_abi_version.argtypes = []
+        L.mla_status_str.restype = ctypes.c_char_p
+        L.mla_status_str.argtypes = [ctypes.c_int32]
+        L.mla_decode_workspace_size.restype = ctypes.c_int
+        L.mla_decode_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+        L.mla_decode.restype = ctypes.c_int
+        L.mla_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.mla_decode_timed.restype = ctypes.c_int
+        L.mla_decode_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp, vp, vp]
+        L.mla_gather_kv.restype = ctypes.c_int
+        L.mla_gather_kv.argtypes = [P, vp, vp, vp, ctypes.c_int32, vp, vp]
+        L.mla_plan_host.restype = ctypes.c_int
+        L.mla_plan_host.argtypes = [P, vp, vp, ctypes.c_int32, i32p, i32p]
+        L.mla_plan_device.restype = ctypes.c_int
+        L.mla_plan_device.argtypes = [P, vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp]
+        L.mla_check_inputs_host.restype = ctypes.c_int
+        L.mla_check_inputs_host.argtypes = [P, vp, vp]
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/libmla.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(mla_\w+)\s*\(", text, re.M)))
+
+
+def mla_abi_version() -> int:
+    return int(lib().mla_abi_version())
+
+
+def status_name(status: int) -> str:
+    try:
+        return lib().mla_status_str(int(status)).decode()
+    except RuntimeError:
+        return str(status)
+
+
+mla_status_str = status_name
+
+
+def _check(status: int, what: str) -> None:
+    if status != MLA_OK:
+        raise MlaError(status, what)
+
+
+def make_params(batch: int, q_len: int, num_heads: int, page_size: int, num_pages: int, block_table_stride: int,
+                max_seq_len: int, kv_dtype: int = MLA_KV_BF16, softmax_scale: float = 1.0, k_scale: float = 1.0,
+                num_splits: int = 0, min_work_units: int = 0, num_cus: int = 0,
+                kv_lora_rank: int = LATENT_DIM, qk_rope_head_dim: int = ROPE_DIM) -> mla_decode_params:
+    return mla_decode_params(int(batch), int(q_len), int(num_heads), int(kv_lora_rank), int(qk_rope_head_dim),
+                             int(page_size), int(num_pages), int(block_table_stride), int(max_seq_len),
+                             int(kv_dtype), float(softmax_scale), float(k_scale), int(num_splits),
+                             int(min_work_units), int(num_cus))
+
+
+def params_for(q, kv_pool, block_table, max_seq_len: int, softmax_scale: float, k_scale: float = 1.0,
+               num_splits: int = 0, min_work_units: int = 0, num_cus: int = 0) -> mla_decode_params:
+    """Parameters read off the tensor shapes of a decode call."""
+    import torch
+    B, ql, H, D = q.shape
+    assert D == ROW_DIM, "query rows must be 576 wide"
+    N, P, Dk = kv_pool.shape
+    assert Dk == ROW_DIM, "pool rows must be 576 wide"
+    fp8 = kv_pool.dtype in (torch.float8_e4m3fn, torch.uint8)
+    return make_params(B, ql, H, P, N, block_table.stride(0) if block_table.dim() == 2 else 1, max_seq_len,
+                       MLA_KV_FP8_E4M3FN if fp8 else MLA_KV_BF16, softmax_scale, k_scale, num_splits,
+                       min_work_units, num_cus)
+
+
+def mla_decode_workspace_size(p: mla_decode_params) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().mla_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)), "mla_decode_workspace_size")
+    return int(n.value)
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else int(t.data_ptr()))
+
+
+def alloc_workspace(p: mla_decode_params, device="cuda"):
+    """A workspace tensor of the size mla_decode needs (torch allocates it)."""
+    import torch
+    n = mla_decode_workspace_size(p)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def mla_decode(q, kv_pool, block_table, seq_lens, out, lse=None, workspace=None, *, max_seq_len: int,
+               softmax_scale: float, k_scale: float = 1.0, num_splits: int = 0, min_work_units: int = 0,
+               stream=None, params: Optional[mla_decode_params] = None):
+    """Enqueue the decode on ``stream`` (default: torch's current stream).
+
+    q [B, q_len, H, 576] bf16; kv_pool [N, P, 576] bf16 or float8_e4m3fn;
+    block_table int32 [B, W]; seq_lens int32 [B]; out [B, q_len, H, 512]
+    bf16; lse fp32 [B, q_len, H] or None; workspace uint8 (allocated here when
+    None).  All on the GPU, contiguous.  Returns (out, lse)."""
+    import torch
+    for name, t in (("q", q), ("kv_pool", kv_pool), ("block_table", block_table), ("seq_lens", seq_lens),
+                    ("out", out)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    if not (q.is_contiguous() and kv_pool.is_contiguous() and out.is_contiguous() and seq_lens.is_contiguous()):
+        raise ValueError("q, kv_pool, seq_lens and out must be contiguous")
+    if block_table.stride(-1) != 1:
+        raise ValueError("block_table rows must be contiguous")
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise ValueError("q and out must be bfloat16")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32")
+    p = params if params is not None else params_for(q, kv_pool, block_table, max_seq_len, softmax_scale, k_scale,
+                                                     num_splits, min_work_units)
+    if workspace is None:
+        workspace = alloc_workspace(p, q.device)
+    st = lib().mla_decode(ctypes.byref(p), _ptr(q), _ptr(kv_pool), _ptr(block_table), _ptr(seq_lens), _ptr(out),
+                          _ptr(lse), _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                          _stream_handle(stream))
+    _check(st, "mla_decode")
+    return out, lse
+
+
+def mla_decode_timed(p: mla_decode_params, q, kv_pool, block_table, seq_lens, out, lse, workspace, stream,
+                     ev_start, ev_split_done, ev_end):
+    """mla_decode with raw hipEvent_t handles (ints, or None) recorded around the two kernels."""
+    st = lib().mla_decode_timed(ctypes.byref(p), _ptr(q), _ptr(kv_pool), _ptr(block_table), _ptr(seq_lens),
+                                _ptr(out), _ptr(lse), _ptr(workspace),
+                                ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                _stream_handle(stream), ctypes.c_void_p(ev_start), ctypes.c_void_p(ev_split_done),
+                                ctypes.c_void_p(ev_end))
+    _check(st, "mla_decode_timed")
+
+
+def mla_gather_kv(p: mla_decode_params, kv_pool, block_table, seq_lens, b: int, dst, stream=None):
+    _check(lib().mla_gather_kv(ctypes.byref(p), _ptr(kv_pool), _ptr(block_table), _ptr(seq_lens), int(b),
+                               _ptr(dst), _stream_handle(stream)), "mla_gather_kv")
+    return dst
+
+
+def mla_plan_host(p: mla_decode_params, seq_lens_host: np.ndarray) -> Tuple[np.ndarray, int]:
+    """The work plan as int32 rows (g, b, row_block, tile_begin, tile_end, slot), and the grid size."""
+    sl = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    n = ctypes.c_int32(0)
+    grid = ctypes.c_int32(0)
+    st = lib().mla_plan_host(ctypes.byref(p), sl.ctypes.data_as(ctypes.c_void_p), None, 0, ctypes.byref(n),
+                             ctypes.byref(grid))
+    if st not in (MLA_OK, MLA_ERR_INVALID_VALUE) or (st == MLA_ERR_INVALID_VALUE and n.value == 0 and p.batch > 0):
+        _check(st, "mla_plan_host")
+    cap = max(n.value, 1)
+    pieces = np.zeros((cap, 6), dtype=np.int32)
+    _check(lib().mla_plan_host(ctypes.byref(p), sl.ctypes.data_as(ctypes.c_void_p),
+                               pieces.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(n), ctypes.byref(grid)),
+           "mla_plan_host")
+    return pieces[:n.value], int(grid.value)
+
+
+def mla_plan_device(p: mla_decode_params, seq_lens_dev, grid: int, max_per_wg: int, stream=None):
+    """The plan as the decode kernel computes it: (pieces [grid, max_per_wg, 6], counts [grid]) on the GPU."""
+    import torch
+    pieces = torch.full((grid, max_per_wg, 6), -7, dtype=torch.int32, device=seq_lens_dev.device)
+    counts = torch.zeros(grid, dtype=torch.int32, device=seq_lens_dev.device)
+    _check(lib().mla_plan_device(ctypes.byref(p), _ptr(seq_lens_dev), _ptr(pieces), int(max_per_wg), _ptr(counts),
+                                 int(grid), _stream_handle(stream)), "mla_plan_device")
+    return pieces, counts
+
+
+def mla_check_inputs_host(p: mla_decode_params, block_table_host: np.ndarray, seq_lens_host: np.ndarray) -> int:
+    bt = np.ascontiguousarray(block_table_host, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    return int(lib().mla_check_inputs_host(ctypes.byref(p), bt.ctypes.data_as(ctypes.c_void_p),
+                                           sl.ctypes.data_as(ctypes.c_void_p)))
+
+
+def algorithmic_work(seq_lens: np.ndarray, q_len: int, heads: int, page_size: int, kv_bytes: int):
+    """(bytes, flops) a decode call must move / compute: every visible KV row
+    once, Q in, O and LSE out, the block-table entries read and seq_lens;
+    QK^T over 576 dims plus P.V over 512 dims for each unmasked (row, token)."""
+    L = np.maximum(np.asarray(seq_lens, dtype=np.int64), 0)
+    B = L.shape[0]
+    n_pages = (L + page_size - 1) // page_size
+    nbytes = int(L.sum()) * ROW_DIM * kv_bytes + B * q_len * heads * (ROW_DIM * 2 + LATENT_DIM * 2 + 4) \
+        + 4 * int(n_pages.sum()) + 4 * B
+    vis = np.maximum(L[:, None] - q_len + 1 + np.arange(q_len)[None, :], 0)
+    flops = 2 * heads * (ROW_DIM + LATENT_DIM) * int(vis.sum())
+    return nbytes, flops

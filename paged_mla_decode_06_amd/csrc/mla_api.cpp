@@ -1,0 +1,339 @@
+// mla_api.cpp -- host side of libmla: argument validation, workspace
+// sizing, the host mirror of the work plan, and the launch sequence.
+//
+// Argument rules follow the decode call of "sglang trtllm_mla_backend.py"
+// (TRTLLMMLABackend._run_decode_kernel: query [B, q_len, H, 576], paged pool
+// [pages, page_size, 576], int32 block tables and seq_lens, max_seq_len,
+// bmm1 scale) and the page-size rule of "tokenspeed trtllm_mla.py"
+// (TRTLLMMLABackend.__init__ rejects page sizes other than 32 and 64).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/libmla.h"
+#include "mla_args.h"
+#include "mla_plan.h"
+
+namespace {
+
+using mla::kRowsPerBlock;
+using mla::kLatentDim;
+
+constexpr int32_t kMaxQLen = 64;
+constexpr int32_t kMaxHeads = 256;
+constexpr int32_t kMaxRows = 4096;
+constexpr int32_t kMaxSplits = 1024;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct DeviceInfo {
+  bool known = false;
+  bool gfx950 = false;
+  int cus = 0;
+};
+
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+mla_status device_info(DeviceInfo* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return MLA_ERR_NOT_SUPPORTED;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!g_dev[dev].known) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MLA_ERR_HIP;
+    g_dev[dev].gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_dev[dev].cus = prop.multiProcessorCount;
+    g_dev[dev].known = true;
+  }
+  *out = g_dev[dev];
+  return MLA_OK;
+}
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.f; }
+
+// Checks that need no device.  Returns MLA_OK or the error.
+mla_status check_params(const mla_decode_params* p) {
+  if (p == nullptr) return MLA_ERR_INVALID_VALUE;
+  if (p->kv_lora_rank != mla::kLatentDim || p->qk_rope_head_dim != mla::kRowDim - mla::kLatentDim)
+    return MLA_ERR_NOT_SUPPORTED;
+  if (p->batch < 0 || p->q_len < 1 || p->num_heads < 1) return MLA_ERR_INVALID_VALUE;
+  if (p->batch > mla::kMaxBatch || p->q_len > kMaxQLen || p->num_heads > kMaxHeads ||
+      (int64_t)p->q_len * p->num_heads > kMaxRows)
+    return MLA_ERR_NOT_SUPPORTED;
+  if (p->page_size != 32 && p->page_size != 64) return MLA_ERR_INVALID_VALUE;
+  if (p->num_pages < 1 || p->max_seq_len < 0 || p->block_table_stride < 1) return MLA_ERR_INVALID_VALUE;
+  if ((int64_t)p->block_table_stride * p->page_size < p->max_seq_len) return MLA_ERR_INVALID_VALUE;
+  if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP8_E4M3FN) return MLA_ERR_INVALID_VALUE;
+  if (!finite_pos(p->softmax_scale)) return MLA_ERR_INVALID_VALUE;
+  if (p->kv_dtype == MLA_KV_FP8_E4M3FN && !finite_pos(p->k_scale)) return MLA_ERR_INVALID_VALUE;
+  if (p->num_splits < 0 || p->num_splits > kMaxSplits) return MLA_ERR_INVALID_VALUE;
+  if (p->min_work_units < 0 || p->num_cus < 0) return MLA_ERR_INVALID_VALUE;
+  // Work units are counted in int32 on the device.
+  const int64_t nrb = mla::row_blocks(p->q_len, p->num_heads);
+  if ((int64_t)p->batch * nrb * mla::units_of(p->max_seq_len) >= ((int64_t)1 << 31)) return MLA_ERR_NOT_SUPPORTED;
+  return MLA_OK;
+}
+
+// Workgroups of the balanced planner, resolving the compute-unit count when needed.
+mla_status target_units(const mla_decode_params* p, int32_t* target) {
+  if (p->min_work_units > 0) {
+    *target = p->min_work_units;
+  } else if (p->num_cus > 0) {
+    *target = p->num_cus;
+  } else {
+    DeviceInfo di;
+    mla_status s = device_info(&di);
+    if (s != MLA_OK) return s;
+    *target = di.cus;
+  }
+  return MLA_OK;
+}
+
+struct Layout {
+  int64_t grid = 0, slots = 0;
+  size_t off_unit = 0, off_lse = 0, off_o = 0, total = 0;
+};
+
+mla_status layout_of(const mla_decode_params* p, Layout* lay) {
+  const int32_t nrb = mla::row_blocks(p->q_len, p->num_heads);
+  int32_t target = 1;
+  if (p->num_splits == 0) {
+    mla_status s = target_units(p, &target);
+    if (s != MLA_OK) return s;
+  }
+  lay->grid = mla::grid_size(p->batch, nrb, p->max_seq_len, p->num_splits, target);
+  lay->slots = mla::slot_count(lay->grid, p->num_splits);
+  lay->off_unit = 0;
+  lay->off_lse = align256(((size_t)p->batch + 1) * sizeof(int32_t));
+  lay->off_o = lay->off_lse + align256((size_t)lay->slots * kRowsPerBlock * sizeof(float));
+  lay->total = lay->off_o + (size_t)lay->slots * kRowsPerBlock * kLatentDim * sizeof(float);
+  if (lay->grid > 0x7fffffff) return MLA_ERR_NOT_SUPPORTED;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_str(int32_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_VALUE: return "MLA_ERR_INVALID_VALUE";
+    case MLA_ERR_NOT_SUPPORTED: return "MLA_ERR_NOT_SUPPORTED";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+mla_status mla_decode_workspace_size(const mla_decode_params* p, size_t* bytes) {
+  if (bytes == nullptr) return MLA_ERR_INVALID_VALUE;
+  mla_status s = check_params(p);
+  if (s != MLA_OK) return s;
+  Layout lay;
+  s = layout_of(p, &lay);
+  if (s != MLA_OK) return s;
+  *bytes = lay.total;
+  return MLA_OK;
+}
+
+static mla_status decode_impl(const mla_decode_params* p, const void* q, const void* kv_pool,
+                              const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream, void* ev_start,
+                              void* ev_mid, void* ev_end) {
+  mla_status s = check_params(p);
+  if (s != MLA_OK) return s;
+  if (p->batch == 0) return MLA_OK;
+  if (q == nullptr || kv_pool == nullptr || block_table == nullptr || seq_lens == nullptr || out == nullptr ||
+      workspace == nullptr)
+    return MLA_ERR_INVALID_VALUE;
+  if (((uintptr_t)q | (uintptr_t)kv_pool | (uintptr_t)out) & 15) return MLA_ERR_INVALID_VALUE;
+  if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_INVALID_VALUE;
+  Layout lay;
+  s = layout_of(p, &lay);
+  if (s != MLA_OK) return s;
+  if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  DeviceInfo di;
+  s = device_info(&di);
+  if (s != MLA_OK) return s;
+  if (!di.gfx950) return MLA_ERR_NOT_SUPPORTED;
+
+  char* ws = (char*)workspace;
+  const bool fp8 = p->kv_dtype == MLA_KV_FP8_E4M3FN;
+  const float kscale = fp8 ? p->k_scale : 1.f;
+  mla::SplitArgs a;
+  a.q = (const uint16_t*)q;
+  a.pool = kv_pool;
+  a.bt = block_table;
+  a.seq_lens = seq_lens;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  a.part_o = (float*)(ws + lay.off_o);
+  a.part_lse = (float*)(ws + lay.off_lse);
+  a.unit_off_ws = (int32_t*)(ws + lay.off_unit);
+  a.B = p->batch;
+  a.q_len = p->q_len;
+  a.H = p->num_heads;
+  a.P = p->page_size;
+  a.W = p->block_table_stride;
+  a.N = p->num_pages;
+  a.max_seq_len = p->max_seq_len;
+  a.nrb = mla::row_blocks(p->q_len, p->num_heads);
+  a.R = p->q_len * p->num_heads;
+  a.num_splits = p->num_splits;
+  a.G = lay.grid;
+  a.scale_log2 = (float)((double)p->softmax_scale * (double)kscale * 1.4426950408889634);
+  a.out_scale = kscale;
+  hipStream_t st = (hipStream_t)stream;
+  if (ev_start != nullptr && hipEventRecord((hipEvent_t)ev_start, st) != hipSuccess) return MLA_ERR_HIP;
+  if (mla_launch_split(&a, fp8 ? 1 : 0, st) != hipSuccess) return MLA_ERR_HIP;
+  if (ev_mid != nullptr && hipEventRecord((hipEvent_t)ev_mid, st) != hipSuccess) return MLA_ERR_HIP;
+  if (p->num_splits != 1) {
+    mla::CombineArgs c;
+    c.part_o = a.part_o;
+    c.part_lse = a.part_lse;
+    c.unit_off_ws = a.unit_off_ws;
+    c.seq_lens = seq_lens;
+    c.out = a.out;
+    c.lse = lse;
+    c.B = a.B;
+    c.q_len = a.q_len;
+    c.H = a.H;
+    c.nrb = a.nrb;
+    c.R = a.R;
+    c.max_seq_len = a.max_seq_len;
+    c.num_splits = a.num_splits;
+    c.G = a.G;
+    if (mla_launch_combine(&c, st) != hipSuccess) return MLA_ERR_HIP;
+  }
+  if (ev_end != nullptr && hipEventRecord((hipEvent_t)ev_end, st) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+mla_status mla_decode(const mla_decode_params* p, const void* q, const void* kv_pool, const int32_t* block_table,
+                      const int32_t* seq_lens, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return decode_impl(p, q, kv_pool, block_table, seq_lens, out, lse, workspace, workspace_bytes, stream, nullptr,
+                     nullptr, nullptr);
+}
+
+mla_status mla_decode_timed(const mla_decode_params* p, const void* q, const void* kv_pool,
+                            const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_split_done,
+                            void* ev_end) {
+  return decode_impl(p, q, kv_pool, block_table, seq_lens, out, lse, workspace, workspace_bytes, stream, ev_start,
+                     ev_split_done, ev_end);
+}
+
+mla_status mla_gather_kv(const mla_decode_params* p, const void* kv_pool, const int32_t* block_table,
+                         const int32_t* seq_lens, int32_t b, void* dst, void* stream) {
+  mla_status s = check_params(p);
+  if (s != MLA_OK) return s;
+  if (kv_pool == nullptr || block_table == nullptr || seq_lens == nullptr || dst == nullptr)
+    return MLA_ERR_INVALID_VALUE;
+  if (b < 0 || b >= p->batch) return MLA_ERR_INVALID_VALUE;
+  if (((uintptr_t)kv_pool | (uintptr_t)dst) & 15) return MLA_ERR_INVALID_VALUE;
+  DeviceInfo di;
+  s = device_info(&di);
+  if (s != MLA_OK) return s;
+  if (!di.gfx950) return MLA_ERR_NOT_SUPPORTED;
+  const int32_t eb = p->kv_dtype == MLA_KV_FP8_E4M3FN ? 1 : 2;
+  if (mla_launch_gather(kv_pool, block_table, seq_lens, p->block_table_stride, p->page_size, p->num_pages,
+                        p->max_seq_len, b, eb, dst, (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+mla_status mla_plan_host(const mla_decode_params* p, const int32_t* seq_lens_host, int32_t* pieces,
+                         int32_t max_pieces, int32_t* n_pieces, int32_t* grid) {
+  mla_status s = check_params(p);
+  if (s != MLA_OK) return s;
+  if (n_pieces == nullptr || grid == nullptr || (p->batch > 0 && seq_lens_host == nullptr)) return MLA_ERR_INVALID_VALUE;
+  if (max_pieces > 0 && pieces == nullptr) return MLA_ERR_INVALID_VALUE;
+  Layout lay;
+  s = layout_of(p, &lay);
+  if (s != MLA_OK) return s;
+  const int32_t B = p->batch, nrb = mla::row_blocks(p->q_len, p->num_heads);
+  const int64_t G = lay.grid;
+  int64_t n = 0;
+  auto emit = [&](int64_t g, const mla::Piece& pc) {
+    if (n < max_pieces) {
+      int32_t* o = pieces + n * 6;
+      o[0] = (int32_t)g; o[1] = pc.b; o[2] = pc.rb; o[3] = pc.tile0; o[4] = pc.tile1; o[5] = pc.slot;
+    }
+    n++;
+  };
+  if (p->num_splits > 0) {
+    for (int64_t g = 0; g < G; g++) {
+      const int64_t blk = g / p->num_splits;
+      const int32_t b = (int32_t)(blk / nrb);
+      mla::Piece pc;
+      if (mla::forced_piece(g, nrb, p->num_splits, mla::units_of(mla::clamp_len(seq_lens_host[b], p->max_seq_len)),
+                            b, &pc))
+        emit(g, pc);
+    }
+  } else {
+    std::vector<int64_t> off((size_t)B + 1, 0);
+    for (int32_t b = 0; b < B; b++)
+      off[b + 1] = off[b] + (int64_t)nrb * mla::units_of(mla::clamp_len(seq_lens_host[b], p->max_seq_len));
+    auto uo = [&](int32_t b) -> int64_t { return off[(size_t)b]; };
+    auto fr = [&](int64_t u) -> int32_t {
+      int32_t lo = 0, hi = B - 1;
+      while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (off[(size_t)mid] <= u) lo = mid; else hi = mid - 1;
+      }
+      return lo;
+    };
+    for (int64_t g = 0; g < G; g++)
+      mla::balanced_pieces(g, G, nrb, uo, fr, B, [&](const mla::Piece& pc) { emit(g, pc); });
+  }
+  *n_pieces = (int32_t)n;
+  *grid = (int32_t)G;
+  return n > max_pieces ? MLA_ERR_INVALID_VALUE : MLA_OK;
+}
+
+mla_status mla_plan_device(const mla_decode_params* p, const int32_t* seq_lens, int32_t* pieces, int32_t max_per_wg,
+                           int32_t* counts, int32_t grid, void* stream) {
+  mla_status s = check_params(p);
+  if (s != MLA_OK) return s;
+  if (seq_lens == nullptr || pieces == nullptr || counts == nullptr || max_per_wg < 1) return MLA_ERR_INVALID_VALUE;
+  Layout lay;
+  s = layout_of(p, &lay);
+  if (s != MLA_OK) return s;
+  if (grid != lay.grid || grid < 1) return MLA_ERR_INVALID_VALUE;
+  DeviceInfo di;
+  s = device_info(&di);
+  if (s != MLA_OK) return s;
+  if (!di.gfx950) return MLA_ERR_NOT_SUPPORTED;
+  if (mla_launch_plan(seq_lens, p->batch, p->max_seq_len, mla::row_blocks(p->q_len, p->num_heads), p->num_splits,
+                      lay.grid, max_per_wg, pieces, counts, (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+mla_status mla_check_inputs_host(const mla_decode_params* p, const int32_t* block_table_host,
+                                 const int32_t* seq_lens_host) {
+  mla_status s = check_params(p);
+  if (s != MLA_OK) return s;
+  if (p->batch > 0 && (block_table_host == nullptr || seq_lens_host == nullptr)) return MLA_ERR_INVALID_VALUE;
+  for (int32_t b = 0; b < p->batch; b++) {
+    const int32_t L = seq_lens_host[b];
+    if (L < 0 || L > p->max_seq_len) return MLA_ERR_INVALID_VALUE;
+    const int32_t n = (L + p->page_size - 1) / p->page_size;
+    for (int32_t i = 0; i < n; i++) {
+      const int32_t pg = block_table_host[(int64_t)b * p->block_table_stride + i];
+      if (pg < 0 || pg >= p->num_pages) return MLA_ERR_INVALID_VALUE;
+    }
+  }
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// mla_args.h -- kernel argument blocks and launchers of libmla (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct SplitArgs {
+  const uint16_t* q;        // [B][q_len][H][576] bf16
+  const void* pool;         // [N][P][576] bf16 or e4m3fn
+  const int32_t* bt;        // [B][W]
+  const int32_t* seq_lens;  // [B]
+  uint16_t* out;            // [B][q_len][H][512] bf16
+  float* lse;               // [B][q_len][H] or null
+  float* part_o;            // [slots][128][512]
+  float* part_lse;          // [slots][128]
+  int32_t* unit_off_ws;     // [B+1] (balanced mode), written by workgroup 0
+  int32_t B, q_len, H, P, W, N, max_seq_len, nrb, R, num_splits;
+  int64_t G;
+  float scale_log2;         // softmax_scale * (k_scale for fp8) * log2(e)
+  float out_scale;          // k_scale for fp8, else 1
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* unit_off_ws;
+  const int32_t* seq_lens;
+  uint16_t* out;
+  float* lse;
+  int32_t B, q_len, H, nrb, R, max_seq_len, num_splits;
+  int64_t G;
+};
+
+}  // namespace mla
+
+extern "C" {
+hipError_t mla_launch_split(const mla::SplitArgs* a, int fp8, hipStream_t stream);
+hipError_t mla_launch_combine(const mla::CombineArgs* a, hipStream_t stream);
+hipError_t mla_launch_gather(const void* pool, const int32_t* bt, const int32_t* seq_lens, int32_t W, int32_t P,
+                             int32_t N, int32_t max_seq_len, int32_t b, int32_t elem_bytes, void* dst,
+                             hipStream_t stream);
+hipError_t mla_launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t nrb, int32_t num_splits,
+                           int64_t G, int32_t max_per_wg, int32_t* pieces, int32_t* counts, hipStream_t stream);
+size_t mla_split_lds_bytes(int32_t B, int32_t num_splits);
+}

@@ -1,0 +1,608 @@
+// mla_kernels.hip -- gfx950 kernels of libmla: split-KV paged MLA decode,
+// LSE combine, debug gather and debug plan.
+//
+// The decode is the one of "sglang trtllm_mla_backend.py"
+// (TRTLLMMLABackend._run_decode_kernel) and "tokenspeed flashmla.py"
+// (FlashMLABackend.forward_decode / forward_extend, causal=True): every
+// query row (j, h) of request b attends over the request's paged 576-wide
+// latent rows; all rows share the one latent KV head, so a KV tile staged
+// once in LDS serves 128 query rows.
+//
+// Split kernel, one workgroup = 4 waves = 64 query rows (one wave per SIMD,
+// so each wave may hold its 16 rows' Q fragments and O accumulators, about
+// 200 registers, with room left for the pipeline); wave w owns rows
+// 16w..16w+15 of the row block, lane l owns row l%16 throughout.  Per
+// 32-token KV tile staged in LDS:
+//   S^T[32 tok x 16 rows]  = K_tile[32 x 576] . Q^T[576 x 16]   (36 MFMA 16x16x32 bf16)
+//   P^T = exp2(S^T*scale*log2e - m)  (online softmax, lazily rescaled)
+//   O^T[512 x 16 rows]    += V^T[512 x 32 tok] . P^T[32 x 16]  (32 MFMA 16x16x32 bf16)
+// With K as the A operand and Q^T as B, the S^T accumulator leaves each lane
+// holding 8 tokens of its own row, which is exactly the B-operand layout P^T
+// needs for the second product, so P never leaves registers and the row max
+// needs two lane exchanges.  V^T comes from the same LDS tile through the
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_args.h"
+#include "mla_plan.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;                      // combine / gather / plan kernels
+// Split kernel shape: kSplitWaves waves of kRowBlocksPerWave 16-row MFMA blocks
+// each; kSplitWaves * kRowBlocksPerWave * 16 == kRowsPerBlock.
+#ifndef MLA_ROWBLOCKS_PER_WAVE
+#define MLA_ROWBLOCKS_PER_WAVE 1
+#endif
+constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
+constexpr int kRowsPerWave = 16 * kRowBlocksPerWave;
+constexpr int kSplitWaves = kRowsPerBlock / kRowsPerWave;
+constexpr int kSplitThreads = 64 * kSplitWaves;
+static_assert(kSplitWaves * kRowsPerWave == kRowsPerBlock, "waves must tile the row block");
+constexpr int kRowBytes = kRowDim * 2;             // 1152: one bf16 row in LDS
+constexpr int kTileBytes = kTile * kRowBytes;      // 36864
+constexpr int kChunks = kTile * kRowDim * 2 / 16;  // 2304 16-byte chunks per bf16 tile
+constexpr int kTileLoads = kChunks / 64;           // 36 wave-wide 1 KB loads per tile
+constexpr int kLoadsPerWave = (kTileLoads + kSplitWaves - 1) / kSplitWaves;   // 5
+constexpr int kQSteps = kRowDim / 32;              // 18 k-steps of 32 over the 576 dims
+constexpr int kVBlocks = kLatentDim / 16;          // 32 blocks of 16 latent dims
+constexpr int kFp8Chunks = kTile * kRowDim / 8;    // 2304 8-byte chunks per fp8 tile
+constexpr int kFp8PerThread = (kFp8Chunks + kSplitThreads - 1) / kSplitThreads;   // 5
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.6931471805599453f;
+// A row's running maximum is raised only when a tile's maximum exceeds it by
+// more than this (log2 units); exponentials stay <= 2^8, exact math unchanged.
+constexpr float kRescaleSlack = 8.0f;
+
+static_assert(kChunks % 64 == 0, "tile must be a whole number of wave-wide loads");
+static_assert(kTile == 32, "the MFMA layout below assumes 32-token tiles");
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// Byte offset of logical 16-byte chunk c of LDS row r.  Chunks are XOR-swizzled
+// inside each 128-byte group by bits 1..3 of the row, which, with the
+// 128-byte shift between odd and even rows, puts the same chunk of 16
+// consecutive rows in 16 different 16-byte bank groups.
+__device__ __forceinline__ int lds_off(int r, int c) {
+  return r * kRowBytes + (((c & ~7) | ((c & 7) ^ ((r >> 1) & 7))) << 4);
+}
+
+// Address of the first element of token t of request b, or null when the
+// block-table entry for t is outside [0, N).  The same addressing serves the
+// decode and the debug gather.
+__device__ __forceinline__ const char* token_row(const void* pool, const int32_t* bt, int32_t W, int32_t P,
+                                                 int32_t N, int32_t b, int32_t t, int32_t elem_bytes) {
+  const int32_t page = bt[(int64_t)b * W + t / P];
+  if ((uint32_t)page >= (uint32_t)N) return nullptr;
+  return (const char*)pool + ((int64_t)page * P + (t % P)) * (int64_t)(kRowDim * elem_bytes);
+}
+
+// ---- KV tile staging.  The 32 rows of a tile are consecutive slots of one
+// page (tiles are 32-token aligned and the page size is 32 or 64), so a tile
+// is one contiguous run of global memory.
+//
+// bf16 pool: each wave issues wave-wide 16-byte loads that write LDS directly
+// (global_load_lds_dwordx4: lane l lands at the wave's LDS base + 16*l); a
+// lane picks the global chunk whose swizzled LDS position is its own.  Lanes
+// of rows past the piece's last token issue no load: those LDS rows keep
+// zeros or an earlier tile's (finite) rows, and their scores are masked.
+template <bool FP8>
+struct Stage;
+
+template <>
+struct Stage<false> {
+  int src_off[kLoadsPerWave];   // byte offset inside the tile's global run
+  int row[kLoadsPerWave];       // tile row this lane's chunk belongs to (>= kTile: no load)
+  __device__ __forceinline__ void init() {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; i++) {
+      const int blk = wave + kSplitWaves * i;
+      const int p = blk * 64 + lane;                 // physical 16-byte chunk of the tile in LDS
+      const int r = p / 72, pc = p - r * 72;
+      const int c = (pc & ~7) | ((pc & 7) ^ ((r >> 1) & 7));   // logical chunk stored there
+      src_off[i] = r * kRowBytes + c * 16;
+      row[i] = blk < kTileLoads ? r : kTile;
+    }
+  }
+  __device__ __forceinline__ void issue(const SplitArgs& a, char* buf, int b, int ts, int tok_end) const {
+    if (ts >= tok_end) return;
+    const int32_t page = __builtin_amdgcn_readfirstlane(a.bt[(int64_t)b * a.W + ts / a.P]);
+    if ((uint32_t)page >= (uint32_t)a.N) return;
+    const char* base = (const char*)a.pool + ((int64_t)page * a.P + (ts % a.P)) * (int64_t)kRowBytes;
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; i++) {
+      char* dst = buf + (wave + kSplitWaves * i) * 1024;
+      if (row[i] < kTile && ts + row[i] < tok_end)
+        __builtin_amdgcn_global_load_lds((const void*)(base + src_off[i]),
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void wait() const { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+};
+
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
+  // e4m3fn -> fp32 is exact; every e4m3fn value is a bf16 value, so keeping
+  // the upper 16 bits of each fp32 is exact too.  The pair is taken as one
+  // 64-bit value and packed with a byte permute: extracting the second float
+  // of the intrinsic's result element-wise was compiled to a copy of the
+  // first one.
+  const u32x2_t f = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_cvt_pk_f32_fp8((int)word, HI));
+  return __builtin_amdgcn_perm(f[1], f[0], 0x07060302u);
+}
+
+// fp8 pool: global -> registers (8 codes per chunk), converted once per tile
+// and stored to LDS as bf16.
+template <>
+struct Stage<true> {
+  u32x2_t v[kFp8PerThread];
+  __device__ __forceinline__ void init() {}
+  __device__ __forceinline__ void load(const SplitArgs& a, int b, int ts, int tok_end) {
+    const char* base = nullptr;
+    if (ts < tok_end) base = token_row(a.pool, a.bt, a.W, a.P, a.N, b, ts, 1);
+#pragma unroll
+    for (int i = 0; i < kFp8PerThread; i++) {
+      const int ci = threadIdx.x + kSplitThreads * i;
+      const int r = ci / 72, c = ci - r * 72;
+      u32x2_t x = {0u, 0u};
+      if (base != nullptr && ci < kFp8Chunks && ts + r < tok_end) x = *(const u32x2_t*)(base + r * kRowDim + c * 8);
+      v[i] = x;
+    }
+  }
+  __device__ __forceinline__ void store(char* buf) const {
+#pragma unroll
+    for (int i = 0; i < kFp8PerThread; i++) {
+      const int ci = threadIdx.x + kSplitThreads * i;
+      if (ci >= kFp8Chunks) continue;
+      const int r = ci / 72, c = ci - r * 72;
+      u32x4_t y;
+      y[0] = fp8x2_to_bf16x2<false>(v[i][0]);
+      y[1] = fp8x2_to_bf16x2<true>(v[i][0]);
+      y[2] = fp8x2_to_bf16x2<false>(v[i][1]);
+      y[3] = fp8x2_to_bf16x2<true>(v[i][1]);
+      *(u32x4_t*)(buf + lds_off(r, c)) = y;
+    }
+  }
+};
+
+__device__ __forceinline__ s16x4_t lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(
+      (__attribute__((address_space(3))) char*)p));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
+// Per-wave running state: kRowBlocksPerWave blocks of 16 rows, lane l owns
+// row l%16 of each block.
+struct RowState {
+  f32x4v_t acc[kRowBlocksPerWave][kVBlocks];   // O^T: row l%16, dims 16*mb + 4*(l/16) + r
+  float m_run[kRowBlocksPerWave];              // running max of the row's scaled scores (log2 units)
+  float l_run[kRowBlocksPerWave];              // this lane's share of the softmax denominator
+};
+
+// One KV tile for one wave: S^T, online softmax, O^T update.  Every K and
+// V^T fragment read from LDS feeds kRowBlocksPerWave MFMAs.
+__device__ __forceinline__ void tile_step(const bf16x8_t (&qf)[kRowBlocksPerWave][kQSteps], RowState& st,
+                                          const char* cur, int ts, const int (&limit)[kRowBlocksPerWave],
+                                          float scale_log2) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, i16 = lane & 15;
+  constexpr int RB = kRowBlocksPerWave;
+  // ---- S^T = K . Q^T, two 16-token blocks
+  f32x4v_t s[RB][2];
+#pragma unroll
+  for (int tb = 0; tb < 2; tb++) {
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++) s[rb][tb] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
+    const int r = 16 * tb + i16;
+    const int rsw = (r >> 1) & 7;
+#pragma unroll
+    for (int k = 0; k < kQSteps; k++) {
+      const int c = 4 * k + g;               // 16-byte chunk holding dims 32k + 8g .. +8
+      const int off = r * kRowBytes + (((c & ~7) | ((c & 7) ^ rsw)) << 4);
+      const bf16x8_t kf = *(const bf16x8_t*)(cur + off);
+#pragma unroll
+      for (int rb = 0; rb < RB; rb++)
+        s[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][k], s[rb][tb], 0, 0, 0);
+    }
+  }
+  // ---- online softmax over the lane's 8 tokens of each of its rows
+  bf16x8_t pf[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++) {
+    float x[8];
+    float mx = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const int t = ts + 16 * (e >> 2) + 4 * g + (e & 3);
+      x[e] = t < limit[rb] ? s[rb][e >> 2][e & 3] * scale_log2 : kNegInf;
+      mx = fmaxf(mx, x[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool need = mx > st.m_run[rb] + kRescaleSlack;
+    if (__any(need)) {
+      const float m_new = need ? mx : st.m_run[rb];
+      const float alpha = need ? __builtin_amdgcn_exp2f(st.m_run[rb] - m_new) : 1.f;   // m_run = -inf gives 0
+      st.l_run[rb] *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < kVBlocks; mb++) st.acc[rb][mb] *= alpha;
+      st.m_run[rb] = m_new;
+    }
+    const float m_use = st.m_run[rb] == kNegInf ? 0.f : st.m_run[rb];
+    float p[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      p[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+      psum += p[e];
+    }
+    st.l_run[rb] += psum;
+    u32x4_t pk;
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+      pk[e] = (uint32_t)f32_to_bf16_rne(p[2 * e]) | ((uint32_t)f32_to_bf16_rne(p[2 * e + 1]) << 16);
+    pf[rb] = __builtin_bit_cast(bf16x8_t, pk);
+  }
+  // ---- O^T += V^T . P^T; the A operand (dims x tokens) via transposing reads:
+  // lane i of 16-lane group g reads 4 dims of token 4g + i/4 (+16); the
+  // hardware hands lane i dim i of the group's 4 tokens.
+  const int vr = 4 * g + (i16 >> 2);
+#pragma unroll
+  for (int mb = 0; mb < kVBlocks; mb++) {
+    const int c = 2 * mb + ((i16 >> 1) & 1);
+    const int o0 = lds_off(vr, c) + 8 * (i16 & 1);
+    const int o1 = lds_off(vr + 16, c) + 8 * (i16 & 1);
+    const u32x2_t lo = __builtin_bit_cast(u32x2_t, lds_read_tr16(cur + o0));
+    const u32x2_t hi = __builtin_bit_cast(u32x2_t, lds_read_tr16(cur + o1));
+    const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++)
+      st.acc[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb], st.acc[rb][mb], 0, 0, 0);
+  }
+}
+
+// One piece: rows [128*rb, 128*rb+128) of request b over tiles [tile0, tile1).
+template <bool FP8>
+__device__ void run_piece(const SplitArgs& a, char* lds, Stage<FP8>& stg, const Piece& pc) {
+  constexpr int RB = kRowBlocksPerWave;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, i16 = lane & 15;
+  const int b = pc.b;
+  const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const int tok_end = min(pc.tile1 * kTile, L);
+  int row_in_blk[RB], jrow[RB], hrow[RB], limit[RB];
+  bool row_ok[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++) {
+    row_in_blk[rb] = wave * kRowsPerWave + 16 * rb + i16;
+    const int row = pc.rb * kRowsPerBlock + row_in_blk[rb];
+    row_ok[rb] = row < a.R;
+    jrow[rb] = row_ok[rb] ? row / a.H : 0;
+    hrow[rb] = row_ok[rb] ? row - jrow[rb] * a.H : 0;
+    limit[rb] = min(tok_end, L - a.q_len + 1 + jrow[rb]);   // tokens t < limit are visible to this row
+  }
+
+  // Q^T B-operand fragments: lane holds row i16 of each block, dims 32k + 8g .. +8.
+  bf16x8_t qf[RB][kQSteps];
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++) {
+    const uint16_t* qrow = a.q + ((int64_t)(b * a.q_len + jrow[rb]) * a.H + hrow[rb]) * kRowDim + 8 * g;
+#pragma unroll
+    for (int k = 0; k < kQSteps; k++) {
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (row_ok[rb]) x = *(const u32x4_t*)(qrow + 32 * k);
+      qf[rb][k] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+  RowState st;
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++) {
+#pragma unroll
+    for (int mb = 0; mb < kVBlocks; mb++) st.acc[rb][mb] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
+    st.m_run[rb] = kNegInf;
+    st.l_run[rb] = 0.f;
+  }
+
+  const int nt = pc.tile1 - pc.tile0;
+  if constexpr (FP8) {
+    stg.load(a, b, pc.tile0 * kTile, tok_end);
+    stg.store(lds);
+    if (nt > 1) stg.load(a, b, (pc.tile0 + 1) * kTile, tok_end);
+    for (int it = 0; it < nt; it++) {
+      __syncthreads();
+      if (it + 1 < nt) stg.store(lds + ((it + 1) & 1) * kTileBytes);
+      if (it + 2 < nt) stg.load(a, b, (pc.tile0 + it + 2) * kTile, tok_end);
+      tile_step(qf, st, lds + (it & 1) * kTileBytes, (pc.tile0 + it) * kTile, limit, a.scale_log2);
+    }
+  } else {
+    stg.issue(a, lds, b, pc.tile0 * kTile, tok_end);
+    for (int it = 0; it < nt; it++) {
+      stg.wait();
+      __syncthreads();
+      if (it + 1 < nt) stg.issue(a, lds + ((it + 1) & 1) * kTileBytes, b, (pc.tile0 + it + 1) * kTile, tok_end);
+      tile_step(qf, st, lds + (it & 1) * kTileBytes, (pc.tile0 + it) * kTile, limit, a.scale_log2);
+    }
+  }
+  __syncthreads();   // the next piece's prologue overwrites the tile buffers
+
+  // ---- epilogue: each row's denominator is spread over the 4 lane groups
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++) {
+    float l_tot = st.l_run[rb] + __shfl_xor(st.l_run[rb], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : a.out_scale / l_tot;
+    const float lse_nat = empty ? kNegInf : (st.m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    if (!row_ok[rb]) continue;
+    if (pc.slot < 0) {
+      const int64_t orow_id = (int64_t)(b * a.q_len + jrow[rb]) * a.H + hrow[rb];
+      uint16_t* orow = a.out + orow_id * kLatentDim;
+#pragma unroll
+      for (int mb = 0; mb < kVBlocks; mb++) {
+        const f32x4v_t v = st.acc[rb][mb] * inv;
+        u32x2_t w;
+        w[0] = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        w[1] = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        *(u32x2_t*)(orow + 16 * mb + 4 * g) = w;
+      }
+      if (a.lse != nullptr && g == 0) a.lse[orow_id] = lse_nat;
+    } else {
+      float* prow = a.part_o + ((int64_t)pc.slot * kRowsPerBlock + row_in_blk[rb]) * kLatentDim;
+#pragma unroll
+      for (int mb = 0; mb < kVBlocks; mb++) *(f32x4v_t*)(prow + 16 * mb + 4 * g) = st.acc[rb][mb] * inv;
+      if (g == 0) a.part_lse[(int64_t)pc.slot * kRowsPerBlock + row_in_blk[rb]] = lse_nat;
+    }
+  }
+}
+
+// Block-wide computation of unit_off[0..B] into LDS (balanced mode).
+template <int NT>
+__device__ void build_unit_offsets(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t nrb,
+                                   int32_t* off) {
+  __shared__ int32_t part[NT];
+  const int tid = threadIdx.x;
+  const int per = (B + NT - 1) / NT;
+  const int b0 = tid * per, b1 = min(B, b0 + per);
+  int32_t sum = 0;
+  for (int b = b0; b < b1; b++) sum += nrb * units_of(clamp_len(seq_lens[b], max_seq_len));
+  part[tid] = sum;
+  __syncthreads();
+  // inclusive scan of part[] (Hillis-Steele)
+  for (int d = 1; d < NT; d <<= 1) {
+    const int32_t v = tid >= d ? part[tid - d] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = tid == 0 ? 0 : part[tid - 1];
+  for (int b = b0; b < b1; b++) {
+    off[b] = run;
+    run += nrb * units_of(clamp_len(seq_lens[b], max_seq_len));
+  }
+  if (tid == NT - 1) off[B] = part[NT - 1];
+  __syncthreads();
+}
+
+__device__ __forceinline__ int32_t find_request(const int32_t* off, int32_t B, int64_t u) {
+  int lo = 0, hi = B - 1;   // largest b with off[b] <= u
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* tiles = smem;
+  int32_t* off = (int32_t*)(smem + 2 * kTileBytes);
+  // Rows a direct load skips keep what is in LDS; start from zeros.
+  for (int i = threadIdx.x; i < 2 * kTileBytes / 16; i += kSplitThreads) ((u32x4_t*)tiles)[i] = u32x4_t{0u, 0u, 0u, 0u};
+  Stage<FP8> stg;
+  stg.init();
+  const int64_t g = blockIdx.x;
+  if (a.num_splits > 0) {
+    __syncthreads();
+    const int64_t blk = g / a.num_splits;
+    const int32_t b = (int32_t)(blk / a.nrb);
+    const int32_t U = units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
+    Piece pc;
+    if (forced_piece(g, a.nrb, a.num_splits, U, b, &pc)) run_piece<FP8>(a, tiles, stg, pc);
+    return;
+  }
+  build_unit_offsets<kSplitThreads>(a.seq_lens, a.B, a.max_seq_len, a.nrb, off);
+  if (g == 0)
+    for (int b = threadIdx.x; b <= a.B; b += kSplitThreads) a.unit_off_ws[b] = off[b];
+  auto uo = [&](int32_t b) -> int64_t { return off[b]; };
+  auto fr = [&](int64_t u) -> int32_t { return find_request(off, a.B, u); };
+  balanced_pieces(g, a.G, a.nrb, uo, fr, a.B, [&](const Piece& pc) { run_piece<FP8>(a, tiles, stg, pc); });
+}
+
+// ---- combine: merge the partial results of each split row block by LSE
+
+
+constexpr int kCombineRowsPerBlock = 16;
+
+__device__ __forceinline__ int64_t combine_slot(const CombineArgs& a, int64_t blk_first_unit, int64_t g,
+                                                int64_t g0) {
+  const int64_t total = a.unit_off_ws[a.B];
+  return (g == g0 && wg_start(g0, total, a.G) != blk_first_unit) ? 2 * g0 + 1 : 2 * g;
+}
+
+__global__ __launch_bounds__(kThreads) void mla_combine_kernel(CombineArgs a) {
+  const int chunks = kRowsPerBlock / kCombineRowsPerBlock;
+  const int64_t blk = blockIdx.x / chunks;     // b * nrb + rb
+  const int chunk = blockIdx.x - (int)(blk * chunks);
+  const int32_t b = (int32_t)(blk / a.nrb), rb = (int32_t)(blk - (int64_t)b * a.nrb);
+  const int32_t U = units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
+  // the pieces of this row block: workgroups [g0, g1] (balanced) or slots blk*S + s (forced)
+  int64_t g0, g1, first_unit = 0, total = 0;
+  if (a.num_splits > 0) {
+    const int32_t Sp = a.num_splits < U ? a.num_splits : U;
+    if (Sp <= 1) return;
+    g0 = blk * a.num_splits;
+    g1 = g0 + Sp - 1;
+  } else {
+    total = a.unit_off_ws[a.B];
+    first_unit = a.unit_off_ws[b] + (int64_t)rb * U;
+    g0 = wg_of_unit(first_unit, total, a.G);
+    g1 = wg_of_unit(first_unit + U - 1, total, a.G);
+    if (g0 == g1) return;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = 0; i < kCombineRowsPerBlock / 4; i++) {
+    const int row_in_blk = chunk * kCombineRowsPerBlock + wave * (kCombineRowsPerBlock / 4) + i;
+    const int row = rb * kRowsPerBlock + row_in_blk;
+    if (row >= a.R) break;
+    float M = kNegInf;
+    for (int64_t g = g0; g <= g1; g++) {
+      if (a.num_splits == 0 && wg_start(g, total, a.G) == wg_start(g + 1, total, a.G)) continue;
+      const int64_t slot = a.num_splits > 0 ? g : combine_slot(a, first_unit, g, g0);
+      M = fmaxf(M, a.part_lse[slot * kRowsPerBlock + row_in_blk]);
+    }
+    f32x4_t o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    if (M != kNegInf) {
+      for (int64_t g = g0; g <= g1; g++) {
+        if (a.num_splits == 0 && wg_start(g, total, a.G) == wg_start(g + 1, total, a.G)) continue;
+        const int64_t slot = a.num_splits > 0 ? g : combine_slot(a, first_unit, g, g0);
+        const float ls = a.part_lse[slot * kRowsPerBlock + row_in_blk];
+        const float w = ls == kNegInf ? 0.f : __expf(ls - M);
+        den += w;
+        const f32x4_t* src = (const f32x4_t*)(a.part_o + (slot * kRowsPerBlock + row_in_blk) * kLatentDim);
+        const f32x4_t v0 = src[2 * lane], v1 = src[2 * lane + 1];
+        o0 += w * v0;
+        o1 += w * v1;
+      }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const int32_t jq = row / a.H, h = row - jq * a.H;
+    const int64_t orow = (int64_t)(b * a.q_len + jq) * a.H + h;
+    u32x4_t w;
+    w[0] = (uint32_t)f32_to_bf16_rne(o0[0] * inv) | ((uint32_t)f32_to_bf16_rne(o0[1] * inv) << 16);
+    w[1] = (uint32_t)f32_to_bf16_rne(o0[2] * inv) | ((uint32_t)f32_to_bf16_rne(o0[3] * inv) << 16);
+    w[2] = (uint32_t)f32_to_bf16_rne(o1[0] * inv) | ((uint32_t)f32_to_bf16_rne(o1[1] * inv) << 16);
+    w[3] = (uint32_t)f32_to_bf16_rne(o1[2] * inv) | ((uint32_t)f32_to_bf16_rne(o1[3] * inv) << 16);
+    *(u32x4_t*)(a.out + orow * kLatentDim + 8 * lane) = w;
+    if (a.lse != nullptr && lane == 0) a.lse[orow] = den > 0.f ? M + __logf(den) : kNegInf;
+  }
+}
+
+// ---- debug: gather one request's stored rows through the block table
+__global__ __launch_bounds__(kThreads) void mla_gather_kernel(const void* pool, const int32_t* bt,
+                                                               const int32_t* seq_lens, int32_t W, int32_t P,
+                                                               int32_t N, int32_t max_seq_len, int32_t b,
+                                                               int32_t elem_bytes, char* dst) {
+  const int32_t L = clamp_len(seq_lens[b], max_seq_len);
+  const int32_t row_bytes = kRowDim * elem_bytes;
+  const int32_t chunks_per_row = row_bytes / 16;
+  const int64_t n = (int64_t)L * chunks_per_row;
+  for (int64_t ci = (int64_t)blockIdx.x * kThreads + threadIdx.x; ci < n; ci += (int64_t)gridDim.x * kThreads) {
+    const int32_t t = (int32_t)(ci / chunks_per_row), c = (int32_t)(ci - (int64_t)t * chunks_per_row);
+    const char* src = token_row(pool, bt, W, P, N, b, t, elem_bytes);
+    u32x4_t x = {0u, 0u, 0u, 0u};
+    if (src != nullptr) x = *(const u32x4_t*)(src + c * 16);
+    *(u32x4_t*)(dst + (int64_t)t * row_bytes + c * 16) = x;
+  }
+}
+
+// ---- debug: the plan as the decode kernel computes it
+__global__ __launch_bounds__(kThreads) void mla_plan_kernel(const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
+                                                             int32_t nrb, int32_t num_splits, int64_t G,
+                                                             int32_t max_per_wg, int32_t* pieces,
+                                                             int32_t* counts) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int32_t* off = (int32_t*)smem;
+  const int64_t g = blockIdx.x;
+  int32_t n = 0;
+  auto emit = [&](const Piece& pc) {
+    if (threadIdx.x == 0 && n < max_per_wg) {
+      int32_t* o = pieces + ((int64_t)g * max_per_wg + n) * 6;
+      o[0] = (int32_t)g; o[1] = pc.b; o[2] = pc.rb; o[3] = pc.tile0; o[4] = pc.tile1; o[5] = pc.slot;
+    }
+    n++;
+  };
+  if (num_splits > 0) {
+    const int64_t blk = g / num_splits;
+    const int32_t b = (int32_t)(blk / nrb);
+    Piece pc;
+    if (forced_piece(g, nrb, num_splits, units_of(clamp_len(seq_lens[b], max_seq_len)), b, &pc)) emit(pc);
+  } else {
+    build_unit_offsets<kThreads>(seq_lens, B, max_seq_len, nrb, off);
+    auto uo = [&](int32_t b) -> int64_t { return off[b]; };
+    auto fr = [&](int64_t u) -> int32_t { return find_request(off, B, u); };
+    balanced_pieces(g, G, nrb, uo, fr, B, emit);
+  }
+  if (threadIdx.x == 0) counts[g] = n;
+}
+
+}  // namespace mla
+
+// ---- launchers called by the host API
+extern "C" {
+
+size_t mla_split_lds_bytes(int32_t B, int32_t num_splits) {
+  return 2 * (size_t)mla::kTileBytes + (num_splits > 0 ? 0 : ((size_t)B + 1) * 4);
+}
+
+hipError_t mla_launch_split(const mla::SplitArgs* a, int fp8, hipStream_t stream) {
+  const size_t lds = mla_split_lds_bytes(a->B, a->num_splits);
+  static bool attr_set[2] = {false, false};
+  if (!attr_set[fp8 ? 1 : 0]) {
+    // dynamic LDS above 64 KB: raise the per-kernel limit once (160 KB per workgroup on gfx950)
+    const void* fn = fp8 ? (const void*)mla::mla_split_kernel<true> : (const void*)mla::mla_split_kernel<false>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 2048);
+    if (e != hipSuccess) return e;
+    attr_set[fp8 ? 1 : 0] = true;
+  }
+  if (fp8)
+    hipLaunchKernelGGL(mla::mla_split_kernel<true>, dim3((unsigned)a->G), dim3(mla::kSplitThreads), lds, stream, *a);
+  else
+    hipLaunchKernelGGL(mla::mla_split_kernel<false>, dim3((unsigned)a->G), dim3(mla::kSplitThreads), lds, stream, *a);
+  return hipGetLastError();
+}
+
+hipError_t mla_launch_combine(const mla::CombineArgs* a, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a->B * a->nrb * (mla::kRowsPerBlock / mla::kCombineRowsPerBlock);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(mla::mla_combine_kernel, dim3((unsigned)blocks), dim3(mla::kThreads), 0, stream, *a);
+  return hipGetLastError();
+}
+
+hipError_t mla_launch_gather(const void* pool, const int32_t* bt, const int32_t* seq_lens, int32_t W, int32_t P,
+                             int32_t N, int32_t max_seq_len, int32_t b, int32_t elem_bytes, void* dst,
+                             hipStream_t stream) {
+  const int64_t chunks = (int64_t)max_seq_len * (mla::kRowDim * elem_bytes / 16);
+  int64_t blocks = (chunks + mla::kThreads - 1) / mla::kThreads;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(mla::mla_gather_kernel, dim3((unsigned)blocks), dim3(mla::kThreads), 0, stream, pool, bt,
+                     seq_lens, W, P, N, max_seq_len, b, elem_bytes, (char*)dst);
+  return hipGetLastError();
+}
+
+hipError_t mla_launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t nrb, int32_t num_splits,
+                           int64_t G, int32_t max_per_wg, int32_t* pieces, int32_t* counts, hipStream_t stream) {
+  const size_t lds = num_splits > 0 ? 16 : ((size_t)B + 1) * 4;
+  hipLaunchKernelGGL(mla::mla_plan_kernel, dim3((unsigned)G), dim3(mla::kThreads), lds, stream, seq_lens, B,
+                     max_seq_len, nrb, num_splits, G, max_per_wg, pieces, counts);
+  return hipGetLastError();
+}
+
+}  // extern "C"

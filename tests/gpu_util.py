@@ -1,0 +1,55 @@
+"""Helpers for the GPU tests: move generator inputs to the device, run the
+decode through the C ABI, compare with the oracle."""
+import numpy as np
+import torch
+
+import paged_mla_decode_06_amd as mla
+
+BF16_TOL = 1e-2   # max|gpu - oracle| <= tol * max|oracle|
+FP8_TOL = 2e-2
+LSE_TOL = 1e-3    # absolute, natural log
+
+
+def to_device(inp, dev="cuda"):
+    q = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    if inp.kv_fp8:
+        pool = torch.from_numpy(inp.pool).view(torch.float8_e4m3fn).to(dev)
+    else:
+        pool = torch.from_numpy(inp.pool.view(np.int16)).view(torch.bfloat16).to(dev)
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    sl = torch.from_numpy(inp.seq_lens).to(dev)
+    return q, pool, bt, sl
+
+
+def run(inp, num_splits=0, min_work_units=None, dev_inputs=None, max_seq_len=None, with_lse=True):
+    """Decode on the GPU; returns (out float32 [B,q,H,512], lse float32 [B,q,H]) on the host."""
+    q, pool, bt, sl = dev_inputs if dev_inputs is not None else to_device(inp)
+    B, ql, H, _ = inp.q.shape
+    out = torch.full((B, ql, H, 512), float("nan"), dtype=torch.bfloat16, device=q.device)
+    lse = torch.full((B, ql, H), float("nan"), dtype=torch.float32, device=q.device) if with_lse else None
+    mwu = inp.workload.min_work_units if min_work_units is None else min_work_units
+    msl = inp.max_seq_len if max_seq_len is None else max_seq_len
+    mla.mla_decode(q, pool, bt, sl, out, lse, max_seq_len=max(msl, 0), softmax_scale=inp.softmax_scale,
+                   k_scale=inp.k_scale, num_splits=num_splits, min_work_units=mwu)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    l = lse.cpu().numpy() if with_lse else None
+    return o, l
+
+
+def compare(o, l, ref_o, ref_l, fp8=False, what=""):
+    tol = FP8_TOL if fp8 else BF16_TOL
+    ref_o = np.asarray(ref_o)
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    scale = float(np.max(np.abs(ref_o))) if ref_o.size else 0.0
+    err = float(np.max(np.abs(o - ref_o))) if ref_o.size else 0.0
+    assert err <= tol * max(scale, 1e-30) or (scale == 0 and err == 0), \
+        f"{what}: max|gpu-oracle| = {err:.3e} > {tol} * {scale:.3e}"
+    if l is not None:
+        ref_l = np.asarray(ref_l)
+        inf = np.isneginf(ref_l)
+        assert np.array_equal(np.isneginf(l), inf), f"{what}: -inf LSE pattern differs"
+        if (~inf).any():
+            lerr = float(np.max(np.abs(l[~inf] - ref_l[~inf])))
+            assert lerr <= LSE_TOL, f"{what}: max|lse err| = {lerr:.3e}"
+    return err / max(scale, 1e-30)

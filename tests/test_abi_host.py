@@ -1,0 +1,151 @@
+"""C ABI on the host (no GPU): the library loads, exports every declared
+symbol, and rejects bad arguments before it touches a device."""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+
+import paged_mla_decode_06_amd as mla
+
+
+@pytest.fixture(scope="module")
+def L():
+    return mla.lib()
+
+
+def good(**kw):
+    base = dict(batch=2, q_len=1, num_heads=16, page_size=64, num_pages=16, block_table_stride=5,
+                max_seq_len=257, kv_dtype=mla.MLA_KV_BF16, softmax_scale=1 / math.sqrt(192), k_scale=1.0,
+                num_splits=0, min_work_units=0, num_cus=256)
+    base.update(kw)
+    return mla.make_params(**base)
+
+
+def test_exports_every_declared_function(L):
+    names = mla.header_functions()
+    assert set(names) >= {"mla_abi_version", "mla_status_str", "mla_decode_workspace_size", "mla_decode",
+                          "mla_gather_kv", "mla_plan_host", "mla_plan_device", "mla_check_inputs_host"}
+    for n in names:
+        assert hasattr(L, n), f"libmla.so does not export {n}"
+
+
+def test_abi_version_and_status_strings(L):
+    assert mla.mla_abi_version() == 1
+    for code, name in [(0, "MLA_OK"), (1, "MLA_ERR_INVALID_VALUE"), (2, "MLA_ERR_NOT_SUPPORTED"),
+                       (3, "MLA_ERR_WORKSPACE_TOO_SMALL"), (4, "MLA_ERR_HIP"), (99, "MLA_ERR_UNKNOWN")]:
+        assert mla.status_name(code) == name
+
+
+def test_params_struct_layout():
+    # 10 int32, 2 float, 3 int32, no padding
+    assert ctypes.sizeof(mla.mla_decode_params) == 15 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page_size=16), mla.MLA_ERR_INVALID_VALUE),            # only 32 and 64
+    (dict(page_size=128), mla.MLA_ERR_INVALID_VALUE),
+    (dict(kv_lora_rank=256), mla.MLA_ERR_NOT_SUPPORTED),
+    (dict(qk_rope_head_dim=32), mla.MLA_ERR_NOT_SUPPORTED),
+    (dict(batch=-1), mla.MLA_ERR_INVALID_VALUE),
+    (dict(q_len=0), mla.MLA_ERR_INVALID_VALUE),
+    (dict(num_heads=0), mla.MLA_ERR_INVALID_VALUE),
+    (dict(q_len=65), mla.MLA_ERR_NOT_SUPPORTED),
+    (dict(num_heads=257), mla.MLA_ERR_NOT_SUPPORTED),
+    (dict(q_len=64, num_heads=128), mla.MLA_ERR_NOT_SUPPORTED),   # q_len*H > 4096
+    (dict(batch=16385), mla.MLA_ERR_NOT_SUPPORTED),
+    (dict(num_pages=0), mla.MLA_ERR_INVALID_VALUE),
+    (dict(max_seq_len=-1), mla.MLA_ERR_INVALID_VALUE),
+    (dict(block_table_stride=4), mla.MLA_ERR_INVALID_VALUE),     # 4*64 < 257
+    (dict(block_table_stride=0), mla.MLA_ERR_INVALID_VALUE),
+    (dict(kv_dtype=7), mla.MLA_ERR_INVALID_VALUE),
+    (dict(softmax_scale=0.0), mla.MLA_ERR_INVALID_VALUE),
+    (dict(softmax_scale=float("nan")), mla.MLA_ERR_INVALID_VALUE),
+    (dict(softmax_scale=float("inf")), mla.MLA_ERR_INVALID_VALUE),
+    (dict(kv_dtype=mla.MLA_KV_FP8_E4M3FN, k_scale=0.0), mla.MLA_ERR_INVALID_VALUE),
+    (dict(kv_dtype=mla.MLA_KV_FP8_E4M3FN, k_scale=float("nan")), mla.MLA_ERR_INVALID_VALUE),
+    (dict(num_splits=-1), mla.MLA_ERR_INVALID_VALUE),
+    (dict(num_splits=1025), mla.MLA_ERR_INVALID_VALUE),
+    (dict(min_work_units=-3), mla.MLA_ERR_INVALID_VALUE),
+    (dict(num_cus=-1), mla.MLA_ERR_INVALID_VALUE),
+])
+def test_invalid_params_rejected(L, kw, status):
+    p = good(**kw)
+    n = ctypes.c_size_t(0)
+    assert L.mla_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+    fake = ctypes.c_void_p(0x1000)
+    assert L.mla_decode(ctypes.byref(p), fake, fake, fake, fake, fake, None, ctypes.c_void_p(0x10000), 1 << 30,
+                        None) == status
+
+
+def test_bf16_pool_ignores_k_scale(L):
+    p = good(k_scale=float("nan"))     # a bf16 pool never reads k_scale
+    assert mla.mla_decode_workspace_size(p) > 0
+
+
+def test_null_and_alignment_checks(L):
+    p = good()
+    fake = ctypes.c_void_p(0x100000)
+    ws = ctypes.c_void_p(0x200000)
+    big = 1 << 34
+    assert L.mla_decode(ctypes.byref(p), None, fake, fake, fake, fake, None, ws, big, None) == mla.MLA_ERR_INVALID_VALUE
+    assert L.mla_decode(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, big, None) == \
+        mla.MLA_ERR_INVALID_VALUE
+    assert L.mla_decode(ctypes.byref(p), ctypes.c_void_p(0x100008), fake, fake, fake, fake, None, ws, big, None) == \
+        mla.MLA_ERR_INVALID_VALUE     # q not 16-byte aligned
+    assert L.mla_decode(ctypes.byref(p), fake, fake, fake, fake, fake, None, ctypes.c_void_p(0x200010), big,
+                        None) == mla.MLA_ERR_INVALID_VALUE     # workspace not 256-byte aligned
+
+
+def test_workspace_too_small_before_any_device_call(L):
+    p = good()
+    need = mla.mla_decode_workspace_size(p)
+    fake = ctypes.c_void_p(0x100000)
+    ws = ctypes.c_void_p(0x200000)
+    assert L.mla_decode(ctypes.byref(p), fake, fake, fake, fake, fake, None, ws, need - 1, None) == \
+        mla.MLA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_empty_batch_is_a_noop(L):
+    p = good(batch=0)
+    assert L.mla_decode(ctypes.byref(p), None, None, None, None, None, None, None, 0, None) == mla.MLA_OK
+
+
+def test_workspace_size_formula():
+    # balanced: grid = min(CUs, B*nrb*units(max)); slots = 2*grid; 64 rows x (512 + 1) floats per slot
+    p = good(batch=64, num_heads=128, max_seq_len=4096, block_table_stride=64, num_cus=256)
+    grid = min(256, 64 * 2 * 128)
+    slots = 2 * grid
+    a256 = lambda x: (x + 255) // 256 * 256
+    expect = a256(65 * 4) + a256(slots * 64 * 4) + slots * 64 * 512 * 4
+    assert mla.mla_decode_workspace_size(p) == expect
+    # forced splits: grid = B*nrb*S, slots = grid
+    p = good(batch=3, num_heads=128, num_splits=5, num_cus=0)
+    grid = 3 * 2 * 5
+    assert mla.mla_decode_workspace_size(p) == a256(4 * 4) + a256(grid * 64 * 4) + grid * 64 * 512 * 4
+
+
+def test_check_inputs_host():
+    from mla_synth import generate
+    inp = generate("tiny")
+    p = good()
+    assert mla.mla_check_inputs_host(p, inp.block_table, inp.seq_lens) == mla.MLA_OK
+    bt = inp.block_table.copy()
+    bt[1, 4] = 16                      # read by tokens 256..257 of request 1
+    assert mla.mla_check_inputs_host(p, bt, inp.seq_lens) == mla.MLA_ERR_INVALID_VALUE
+    bt = inp.block_table.copy()
+    bt[0, 2] = 99                      # past request 0's last page: never read
+    assert mla.mla_check_inputs_host(p, bt, inp.seq_lens) == mla.MLA_OK
+    sl = inp.seq_lens.copy()
+    sl[0] = 258                        # above max_seq_len
+    assert mla.mla_check_inputs_host(p, inp.block_table, sl) == mla.MLA_ERR_INVALID_VALUE
+    sl[0] = -1
+    assert mla.mla_check_inputs_host(p, inp.block_table, sl) == mla.MLA_ERR_INVALID_VALUE
+
+
+def test_algorithmic_work_formula():
+    nbytes, flops = mla.algorithmic_work(np.array([100, 257]), 1, 16, 64, 2)
+    assert nbytes == 357 * 576 * 2 + 2 * 16 * (1152 + 1024 + 4) + 4 * (2 + 5) + 8
+    assert flops == 2 * 16 * 1088 * 357
+    _, f4 = mla.algorithmic_work(np.array([10]), 4, 1, 64, 2)
+    assert f4 == 2 * 1088 * (7 + 8 + 9 + 10)

@@ -1,0 +1,82 @@
+"""GPU decode vs the CPU oracle (through the C ABI), element by element.
+
+Small inputs are compared in full; the full-size workloads, in the launch
+configuration the benchmark times, are compared on sampled query rows that
+the oracle computes one by one, plus properties that hold at any size."""
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle
+import oracle_pins as P
+from mla_synth import generate, WORKLOADS
+import gpu_util as G
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def test_tiny_workload(orc):
+    inp = generate("tiny")
+    o, l = G.run(inp)
+    ro, rl = orc.decode(inp)
+    G.compare(o, l, ro, rl, what="tiny")
+
+
+CASES = [
+    # kv, q_len, heads, page, lens
+    ("bf16", 1, 16, 64, (1, 31, 32, 33, 63, 64, 65, 100, 257)),
+    ("bf16", 1, 128, 32, (5, 300, 1000)),
+    ("bf16", 1, 64, 64, (0, 1, 2, 129)),
+    ("bf16", 1, 1, 32, (40, 90)),
+    ("bf16", 1, 48, 64, (77, 1)),
+    ("bf16", 4, 128, 64, (4, 5, 67, 300)),
+    ("bf16", 2, 16, 32, (1, 2, 3, 40)),
+    ("bf16", 3, 40, 64, (2, 3, 97)),
+    ("fp8", 1, 128, 64, (1, 64, 65, 500)),
+    ("fp8", 1, 16, 32, (0, 33, 100)),
+    ("fp8", 4, 32, 64, (4, 70, 131)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("mode", ["balanced", "balanced8", "split3"])
+def test_small_cases(orc, case, mode):
+    kv, ql, H, Pg, lens = CASES[case]
+    inp = P.small(kv=kv, q_len=ql, heads=H, page_size=Pg, lens=lens, seed=100 + case)
+    kw = dict(balanced=dict(), balanced8=dict(min_work_units=8), split3=dict(num_splits=3))[mode]
+    o, l = G.run(inp, **kw)
+    ro, rl = orc.decode(inp)
+    G.compare(o, l, ro, rl, fp8=kv == "fp8", what=f"{CASES[case]} {mode}")
+
+
+def _sample_rows(inp, n_per_req, seed):
+    rng = np.random.default_rng(seed)
+    sel = []
+    for b in range(inp.batch):
+        for _ in range(n_per_req):
+            sel.append((b, int(rng.integers(inp.q_len)), int(rng.integers(inp.heads))))
+        sel.append((b, inp.q_len - 1, inp.heads - 1))
+    return sel
+
+
+@pytest.mark.parametrize("name", ["deepseek_decode", "long_context", "mtp_verify", "fp8_kv"])
+def test_full_size_workload_sampled(orc, name):
+    inp = generate(name)
+    o, l = G.run(inp)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    per = {"deepseek_decode": 4, "long_context": 24, "mtp_verify": 1, "fp8_kv": 1}[name]
+    sel = _sample_rows(inp, per, seed=7)
+    ro, rl = orc.decode_rows(inp, sel)
+    go = np.stack([o[b, j, h] for b, j, h in sel])
+    gl = np.array([l[b, j, h] for b, j, h in sel])
+    G.compare(go, gl, ro, rl, fp8=inp.kv_fp8, what=name)

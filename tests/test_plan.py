@@ -1,0 +1,97 @@
+"""The split-KV work plan on the host (no GPU): every (request, row block)
+is covered exactly once, partial slots are unique, the balanced grid is
+evenly loaded."""
+import math
+
+import numpy as np
+import pytest
+
+import paged_mla_decode_06_amd as mla
+
+
+def params(B, q_len, H, max_len, num_splits=0, min_work_units=0, num_cus=256, P=64):
+    W = max(1, -(-max_len // P))
+    return mla.make_params(B, q_len, H, P, 1 << 20, W, max_len, mla.MLA_KV_BF16, 0.07, 1.0, num_splits,
+                           min_work_units, num_cus)
+
+
+def check_cover(p, L, pieces, grid):
+    B, nrb = p.batch, -(-p.q_len * p.num_heads // mla.ROWS_PER_BLOCK)
+    U = np.maximum(1, -(-np.clip(L, 0, p.max_seq_len) // mla.TILE))
+    cover = {}
+    for g, b, rb, t0, t1, slot in pieces:
+        assert 0 <= g < grid and 0 <= b < B and 0 <= rb < nrb and 0 <= t0 < t1 <= U[b]
+        cover.setdefault((b, rb), []).append((t0, t1, slot, g))
+    assert len(cover) == B * nrb
+    used = set()
+    for (b, rb), lst in cover.items():
+        lst.sort()
+        assert lst[0][0] == 0 and lst[-1][1] == U[b]
+        for (a0, a1, _, _), (c0, _, _, _) in zip(lst, lst[1:]):
+            assert a1 == c0, "pieces must tile the range without gaps or overlap"
+        if len(lst) == 1:
+            assert lst[0][2] == -1, "a whole row block writes the output directly"
+        else:
+            for _, _, slot, _ in lst:
+                assert slot >= 0 and slot not in used
+                used.add(slot)
+    return cover
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_balanced_plan_covers_and_balances(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 300))
+    q_len = int(rng.choice([1, 2, 4]))
+    H = int(rng.choice([16, 64, 128]))
+    L = rng.integers(0, 5000, size=B).astype(np.int32)
+    if seed == 0:
+        L[:] = 0
+    p = params(B, q_len, H, int(max(L.max(), 1)), num_cus=int(rng.choice([8, 256, 512])))
+    pieces, grid = mla.mla_plan_host(p, L)
+    check_cover(p, L, pieces, grid)
+    # each workgroup's units differ by at most one
+    units = np.zeros(grid, dtype=np.int64)
+    for g, b, rb, t0, t1, slot in pieces:
+        units[g] += t1 - t0
+    assert units.max() - units.min() <= 1
+    # at most two partial pieces per workgroup
+    part = np.zeros(grid, dtype=np.int64)
+    for g, b, rb, t0, t1, slot in pieces:
+        part[g] += slot >= 0
+    assert part.max() <= 2
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 64])
+def test_forced_plan(S):
+    L = np.array([0, 1, 31, 32, 33, 300, 4096], dtype=np.int32)
+    p = params(len(L), 1, 128, 4096, num_splits=S)
+    pieces, grid = mla.mla_plan_host(p, L)
+    assert grid == len(L) * 2 * S
+    cover = check_cover(p, L, pieces, grid)
+    for (b, rb), lst in cover.items():
+        U = max(1, -(-int(L[b]) // 32))
+        assert len(lst) == min(S, U)
+
+
+def test_grid_follows_cu_count_and_min_units():
+    L = np.full(8, 32768, dtype=np.int32)
+    _, grid = mla.mla_plan_host(params(8, 1, 128, 32768, num_cus=256), L)
+    assert grid == 256
+    _, grid = mla.mla_plan_host(params(8, 1, 128, 32768, min_work_units=512, num_cus=256), L)
+    assert grid == 512
+    # never more workgroups than units
+    _, grid = mla.mla_plan_host(params(2, 1, 16, 100, num_cus=256), np.array([100, 50], dtype=np.int32))
+    assert grid == 2 * 1 * 4
+
+
+def test_long_context_workload_plan():
+    """The long-context workload asks for at least 2x the CU count of work units."""
+    from mla_synth import WORKLOADS
+    from mla_synth.gen import draw_seq_lens
+    w = WORKLOADS["long_context"]
+    L = draw_seq_lens(w, np.random.default_rng(w.seed))
+    p = params(w.batch, 1, w.heads, 32768, min_work_units=w.min_work_units, P=32)
+    pieces, grid = mla.mla_plan_host(p, L)
+    assert grid >= 512
+    check_cover(p, L, pieces, grid)
