@@ -33,7 +33,7 @@
  *    lie in [0, max_seq_len] (values outside are clamped), and every
  *    block-table entry a request reads (index < ceil(seq_lens[b] /
  *    page_size)) must lie in [0, num_pages).  An entry outside that range is
- *    read as a page of zeros, never dereferenced.  Entries past a request's
+ *    never dereferenced (that tile is skipped, and the result is undefined).  Entries past a request's
  *    last page are never read and may hold anything (-1, 0, ...).
  *    mla_check_inputs_host() checks all of this on host copies.
  *  - A workspace must not be shared by calls that may run concurrently.
@@ -64,7 +64,7 @@ typedef enum {
 } mla_kv_dtype;
 
 typedef struct {
-  int32_t batch;              /* B >= 0 requests; B = 0 enqueues nothing. At most 16384. */
+  int32_t batch;              /* B >= 0 requests; B = 0 enqueues nothing. At most 8192. */
   int32_t q_len;              /* query tokens per request, 1..64 (q_len > 1: causal, bottom-right aligned) */
   int32_t num_heads;          /* H query heads per request (this GPU's share), 1..256; q_len*H <= 4096 */
   int32_t kv_lora_rank;       /* must be 512 (latent width = output width per head) */

@@ -18,6 +18,10 @@ SOURCES = ["mla_kernels.hip", "mla_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", INCLUDE, "-I", CSRC,
           # no packed fp32 instructions in any device code
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMA accumulators in VGPRs: the O accumulators are rescaled by VALU
+          # code, which cannot touch AGPRs; the Q fragments (read-only MFMA
+          # operands) then take the AGPRs
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wall", "-Wno-unused-function"]
 
 

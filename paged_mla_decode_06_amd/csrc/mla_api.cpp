@@ -95,7 +95,7 @@ mla_status target_units(const mla_decode_params* p, int32_t* target) {
 }
 
 struct Layout {
-  int64_t grid = 0, slots = 0;
+  int64_t groups = 0, wgs = 0, slots = 0;
   size_t off_unit = 0, off_lse = 0, off_o = 0, total = 0;
 };
 
@@ -106,13 +106,14 @@ mla_status layout_of(const mla_decode_params* p, Layout* lay) {
     mla_status s = target_units(p, &target);
     if (s != MLA_OK) return s;
   }
-  lay->grid = mla::grid_size(p->batch, nrb, p->max_seq_len, p->num_splits, target);
-  lay->slots = mla::slot_count(lay->grid, p->num_splits);
+  lay->groups = mla::group_count(p->batch, nrb, p->max_seq_len, p->num_splits, target);
+  lay->wgs = lay->groups * nrb;
+  lay->slots = mla::slot_count(lay->groups, nrb, p->num_splits);
   lay->off_unit = 0;
   lay->off_lse = align256(((size_t)p->batch + 1) * sizeof(int32_t));
   lay->off_o = lay->off_lse + align256((size_t)lay->slots * kRowsPerBlock * sizeof(float));
-  lay->total = lay->off_o + (size_t)lay->slots * kRowsPerBlock * kLatentDim * sizeof(float);
-  if (lay->grid > 0x7fffffff) return MLA_ERR_NOT_SUPPORTED;
+  lay->total = lay->off_o + (size_t)lay->slots * kRowsPerBlock * kLatentDim * sizeof(uint16_t);
+  if (mla::launch_grid(lay->groups, nrb) > 0x7fffffff) return MLA_ERR_NOT_SUPPORTED;
   return MLA_OK;
 }
 
@@ -175,7 +176,7 @@ static mla_status decode_impl(const mla_decode_params* p, const void* q, const v
   a.seq_lens = seq_lens;
   a.out = (uint16_t*)out;
   a.lse = lse;
-  a.part_o = (float*)(ws + lay.off_o);
+  a.part_o = (uint16_t*)(ws + lay.off_o);
   a.part_lse = (float*)(ws + lay.off_lse);
   a.unit_off_ws = (int32_t*)(ws + lay.off_unit);
   a.B = p->batch;
@@ -188,7 +189,7 @@ static mla_status decode_impl(const mla_decode_params* p, const void* q, const v
   a.nrb = mla::row_blocks(p->q_len, p->num_heads);
   a.R = p->q_len * p->num_heads;
   a.num_splits = p->num_splits;
-  a.G = lay.grid;
+  a.NG = lay.groups;
   a.scale_log2 = (float)((double)p->softmax_scale * (double)kscale * 1.4426950408889634);
   a.out_scale = kscale;
   hipStream_t st = (hipStream_t)stream;
@@ -210,7 +211,7 @@ static mla_status decode_impl(const mla_decode_params* p, const void* q, const v
     c.R = a.R;
     c.max_seq_len = a.max_seq_len;
     c.num_splits = a.num_splits;
-    c.G = a.G;
+    c.NG = a.NG;
     if (mla_launch_combine(&c, st) != hipSuccess) return MLA_ERR_HIP;
   }
   if (ev_end != nullptr && hipEventRecord((hipEvent_t)ev_end, st) != hipSuccess) return MLA_ERR_HIP;
@@ -261,28 +262,28 @@ mla_status mla_plan_host(const mla_decode_params* p, const int32_t* seq_lens_hos
   s = layout_of(p, &lay);
   if (s != MLA_OK) return s;
   const int32_t B = p->batch, nrb = mla::row_blocks(p->q_len, p->num_heads);
-  const int64_t G = lay.grid;
+  const int64_t NG = lay.groups;
   int64_t n = 0;
-  auto emit = [&](int64_t g, const mla::Piece& pc) {
+  auto emit = [&](const mla::Piece& pc, int64_t wg) {
     if (n < max_pieces) {
       int32_t* o = pieces + n * 6;
-      o[0] = (int32_t)g; o[1] = pc.b; o[2] = pc.rb; o[3] = pc.tile0; o[4] = pc.tile1; o[5] = pc.slot;
+      o[0] = (int32_t)wg; o[1] = pc.b; o[2] = pc.rb; o[3] = pc.tile0; o[4] = pc.tile1; o[5] = pc.slot;
     }
     n++;
   };
   if (p->num_splits > 0) {
-    for (int64_t g = 0; g < G; g++) {
-      const int64_t blk = g / p->num_splits;
-      const int32_t b = (int32_t)(blk / nrb);
-      mla::Piece pc;
-      if (mla::forced_piece(g, nrb, p->num_splits, mla::units_of(mla::clamp_len(seq_lens_host[b], p->max_seq_len)),
-                            b, &pc))
-        emit(g, pc);
-    }
+    for (int64_t g = 0; g < NG; g++)
+      for (int32_t rb = 0; rb < nrb; rb++) {
+        const int32_t b = (int32_t)(g / p->num_splits);
+        mla::Piece pc;
+        if (mla::forced_piece(g, rb, nrb, p->num_splits,
+                              mla::units_of(mla::clamp_len(seq_lens_host[b], p->max_seq_len)), &pc))
+          emit(pc, g * nrb + rb);
+      }
   } else {
     std::vector<int64_t> off((size_t)B + 1, 0);
     for (int32_t b = 0; b < B; b++)
-      off[b + 1] = off[b] + (int64_t)nrb * mla::units_of(mla::clamp_len(seq_lens_host[b], p->max_seq_len));
+      off[b + 1] = off[b] + mla::units_of(mla::clamp_len(seq_lens_host[b], p->max_seq_len));
     auto uo = [&](int32_t b) -> int64_t { return off[(size_t)b]; };
     auto fr = [&](int64_t u) -> int32_t {
       int32_t lo = 0, hi = B - 1;
@@ -292,11 +293,12 @@ mla_status mla_plan_host(const mla_decode_params* p, const int32_t* seq_lens_hos
       }
       return lo;
     };
-    for (int64_t g = 0; g < G; g++)
-      mla::balanced_pieces(g, G, nrb, uo, fr, B, [&](const mla::Piece& pc) { emit(g, pc); });
+    for (int64_t g = 0; g < NG; g++)
+      for (int32_t rb = 0; rb < nrb; rb++)
+        mla::balanced_pieces(g, NG, rb, nrb, uo, fr, B, [&](const mla::Piece& pc) { emit(pc, g * nrb + rb); });
   }
   *n_pieces = (int32_t)n;
-  *grid = (int32_t)G;
+  *grid = (int32_t)lay.wgs;
   return n > max_pieces ? MLA_ERR_INVALID_VALUE : MLA_OK;
 }
 
@@ -308,13 +310,13 @@ mla_status mla_plan_device(const mla_decode_params* p, const int32_t* seq_lens, 
   Layout lay;
   s = layout_of(p, &lay);
   if (s != MLA_OK) return s;
-  if (grid != lay.grid || grid < 1) return MLA_ERR_INVALID_VALUE;
+  if (grid != lay.wgs || grid < 1) return MLA_ERR_INVALID_VALUE;
   DeviceInfo di;
   s = device_info(&di);
   if (s != MLA_OK) return s;
   if (!di.gfx950) return MLA_ERR_NOT_SUPPORTED;
   if (mla_launch_plan(seq_lens, p->batch, p->max_seq_len, mla::row_blocks(p->q_len, p->num_heads), p->num_splits,
-                      lay.grid, max_per_wg, pieces, counts, (hipStream_t)stream) != hipSuccess)
+                      lay.groups, max_per_wg, pieces, counts, (hipStream_t)stream) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -12,24 +12,24 @@ struct SplitArgs {
   const int32_t* seq_lens;  // [B]
   uint16_t* out;            // [B][q_len][H][512] bf16
   float* lse;               // [B][q_len][H] or null
-  float* part_o;            // [slots][128][512]
-  float* part_lse;          // [slots][128]
+  uint16_t* part_o;         // [slots][64][512] bf16, normalised partial outputs
+  float* part_lse;          // [slots][64]
   int32_t* unit_off_ws;     // [B+1] (balanced mode), written by workgroup 0
   int32_t B, q_len, H, P, W, N, max_seq_len, nrb, R, num_splits;
-  int64_t G;
+  int64_t NG;   // groups of the plan
   float scale_log2;         // softmax_scale * (k_scale for fp8) * log2(e)
   float out_scale;          // k_scale for fp8, else 1
 };
 
 struct CombineArgs {
-  const float* part_o;
+  const uint16_t* part_o;
   const float* part_lse;
   const int32_t* unit_off_ws;
   const int32_t* seq_lens;
   uint16_t* out;
   float* lse;
   int32_t B, q_len, H, nrb, R, max_seq_len, num_splits;
-  int64_t G;
+  int64_t NG;   // groups of the plan
 };
 
 }  // namespace mla

@@ -63,9 +63,17 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
 
 static_assert(kChunks % 64 == 0, "tile must be a whole number of wave-wide loads");
+static_assert(kTileLoads % kSplitWaves == 0, "every wave issues the same number of tile loads");
+static_assert(kLoadsPerWave == 9, "the vmcnt immediates in Stage<false>::wait assume 9 loads per wave and tile");
+// KV tile buffers in LDS: kTileBufs - 1 tiles are in flight while one is consumed.
+constexpr int kTileBufs = 3;
 static_assert(kTile == 32, "the MFMA layout below assumes 32-token tiles");
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+// Pointers into LDS carry the LDS address space, so that address arithmetic
+// stays 32-bit and constant offsets fold into the DS instructions.
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) const char lds_cchar;
 
 // Byte offset of logical 16-byte chunk c of LDS row r.  Chunks are XOR-swizzled
 // inside each 128-byte group by bits 1..3 of the row, which, with the
@@ -85,6 +93,30 @@ __device__ __forceinline__ const char* token_row(const void* pool, const int32_t
   return (const char*)pool + ((int64_t)page * P + (t % P)) * (int64_t)(kRowDim * elem_bytes);
 }
 
+// Block-table entries of one request, 64 at a time in one vector register
+// (lane l holds entry first + l), so a tile's page id is a lane read rather
+// than a memory load whose wait would also drain the tile loads in flight.
+// Only entries of pages the piece reads are loaded.
+struct PageWindow {
+  int32_t vec = -1;
+  int32_t first = 0;
+  int32_t end = 0;     // one past the last entry the piece reads
+  __device__ __forceinline__ void load(const SplitArgs& a, int b, int first_entry) {
+    first = first_entry;
+    const int lane = threadIdx.x & 63;
+    vec = first + lane < end ? a.bt[(int64_t)b * a.W + first + lane] : -1;
+  }
+  __device__ __forceinline__ void init(const SplitArgs& a, int b, int first_entry, int end_entry) {
+    end = end_entry;
+    load(a, b, first_entry);
+  }
+  // page id of block-table entry idx (first <= idx < end), uniform across the wave
+  __device__ __forceinline__ int32_t page(const SplitArgs& a, int b, int idx) {
+    if (idx - first >= 64) load(a, b, idx);
+    return __builtin_amdgcn_readlane(vec, idx - first);
+  }
+};
+
 // ---- KV tile staging.  The 32 rows of a tile are consecutive slots of one
 // page (tiles are 32-token aligned and the page size is 32 or 64), so a tile
 // is one contiguous run of global memory.
@@ -100,7 +132,7 @@ struct Stage;
 template <>
 struct Stage<false> {
   int src_off[kLoadsPerWave];   // byte offset inside the tile's global run
-  int row[kLoadsPerWave];       // tile row this lane's chunk belongs to (>= kTile: no load)
+  int row[kLoadsPerWave];       // tile row this lane's chunk belongs to
   __device__ __forceinline__ void init() {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -110,24 +142,36 @@ struct Stage<false> {
       const int r = p / 72, pc = p - r * 72;
       const int c = (pc & ~7) | ((pc & 7) ^ ((r >> 1) & 7));   // logical chunk stored there
       src_off[i] = r * kRowBytes + c * 16;
-      row[i] = blk < kTileLoads ? r : kTile;
+      row[i] = r;
     }
   }
-  __device__ __forceinline__ void issue(const SplitArgs& a, char* buf, int b, int ts, int tok_end) const {
+  // Issues exactly kLoadsPerWave loads per wave for a tile that holds at
+  // least one valid token (the waits below count on it); rows past the last
+  // valid token re-read the tile's first row, so every LDS row stays finite.
+  // A tile with no valid token (only a request with no token at all) or a
+  // block-table entry outside [0, N) issues nothing.
+  __device__ __forceinline__ void issue(const SplitArgs& a, lds_char* buf, PageWindow& pw, int b, int ts,
+                                        int tok_end) const {
     if (ts >= tok_end) return;
-    const int32_t page = __builtin_amdgcn_readfirstlane(a.bt[(int64_t)b * a.W + ts / a.P]);
+    const int32_t page = pw.page(a, b, ts / a.P);
     if ((uint32_t)page >= (uint32_t)a.N) return;
     const char* base = (const char*)a.pool + ((int64_t)page * a.P + (ts % a.P)) * (int64_t)kRowBytes;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool full = ts + kTile <= tok_end;
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; i++) {
-      char* dst = buf + (wave + kSplitWaves * i) * 1024;
-      if (row[i] < kTile && ts + row[i] < tok_end)
-        __builtin_amdgcn_global_load_lds((const void*)(base + src_off[i]),
-                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      lds_char* dst = buf + (wave + kSplitWaves * i) * 1024;
+      const int off = full || ts + row[i] < tok_end ? src_off[i] : src_off[i] - row[i] * kRowBytes;
+      __builtin_amdgcn_global_load_lds((const void*)(base + off), (__attribute__((address_space(3))) void*)dst, 16,
+                                       0, 0);
     }
   }
-  __device__ __forceinline__ void wait() const { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+  // Wait until at most `later` tiles' loads (issued after this tile's) are in flight.
+  __device__ __forceinline__ void wait(int later) const {
+    if (later >= 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
 };
 
 template <bool HI>
@@ -147,9 +191,12 @@ template <>
 struct Stage<true> {
   u32x2_t v[kFp8PerThread];
   __device__ __forceinline__ void init() {}
-  __device__ __forceinline__ void load(const SplitArgs& a, int b, int ts, int tok_end) {
+  __device__ __forceinline__ void load(const SplitArgs& a, PageWindow& pw, int b, int ts, int tok_end) {
     const char* base = nullptr;
-    if (ts < tok_end) base = token_row(a.pool, a.bt, a.W, a.P, a.N, b, ts, 1);
+    if (ts < tok_end) {
+      const int32_t page = pw.page(a, b, ts / a.P);
+      if ((uint32_t)page < (uint32_t)a.N) base = (const char*)a.pool + ((int64_t)page * a.P + (ts % a.P)) * kRowDim;
+    }
 #pragma unroll
     for (int i = 0; i < kFp8PerThread; i++) {
       const int ci = threadIdx.x + kSplitThreads * i;
@@ -159,7 +206,7 @@ struct Stage<true> {
       v[i] = x;
     }
   }
-  __device__ __forceinline__ void store(char* buf) const {
+  __device__ __forceinline__ void store(lds_char* buf) const {
 #pragma unroll
     for (int i = 0; i < kFp8PerThread; i++) {
       const int ci = threadIdx.x + kSplitThreads * i;
@@ -170,14 +217,13 @@ struct Stage<true> {
       y[1] = fp8x2_to_bf16x2<true>(v[i][0]);
       y[2] = fp8x2_to_bf16x2<false>(v[i][1]);
       y[3] = fp8x2_to_bf16x2<true>(v[i][1]);
-      *(u32x4_t*)(buf + lds_off(r, c)) = y;
+      *(__attribute__((address_space(3))) u32x4_t*)(buf + lds_off(r, c)) = y;
     }
   }
 };
 
-__device__ __forceinline__ s16x4_t lds_read_tr16(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(
-      (__attribute__((address_space(3))) char*)p));
+__device__ __forceinline__ s16x4_t lds_read_tr16(lds_cchar* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -194,56 +240,100 @@ struct RowState {
   float l_run[kRowBlocksPerWave];              // this lane's share of the softmax denominator
 };
 
-// One KV tile for one wave: S^T, online softmax, O^T update.  Every K and
-// V^T fragment read from LDS feeds kRowBlocksPerWave MFMAs.
-__device__ __forceinline__ void tile_step(const bf16x8_t (&qf)[kRowBlocksPerWave][kQSteps], RowState& st,
-                                          const char* cur, int ts, const int (&limit)[kRowBlocksPerWave],
-                                          float scale_log2) {
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4, i16 = lane & 15;
-  constexpr int RB = kRowBlocksPerWave;
-  // ---- S^T = K . Q^T, two 16-token blocks
-  f32x4v_t s[RB][2];
+constexpr int kQKSteps = 2 * kQSteps;   // (token block, k-step) pairs of S^T = K . Q^T
+
+// Lane-dependent parts of the LDS addresses a wave reads, fixed for the
+// whole kernel; every per-read remainder is a compile-time offset.
+//  K fragment of step s = 2k + tb: token 16tb + l%16, dims 32k + 8(l/16)..+8,
+//    at kbase[k&1] + 18432*tb + 128*(k>>1).
+//  V^T block mb (two transposing reads): lane i of 16-lane group g reads
+//    4 dims of token 4g + i/4 (and of token 16 + 4g + i/4); the hardware hands
+//    lane i dim 16mb + i of the group's 4 tokens.  At vbase[mb&3] +
+//    18432*second + 128*(mb>>2).
+struct LaneOffsets {
+  int kbase[2];
+  int vbase[4];
+  __device__ __forceinline__ void init() {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, i16 = lane & 15;
+    const int zk = (i16 >> 1) & 7;                       // swizzle of rows i16 and 16 + i16
 #pragma unroll
-  for (int tb = 0; tb < 2; tb++) {
+    for (int p = 0; p < 2; p++) kbase[p] = i16 * kRowBytes + 16 * ((g + 4 * p) ^ zk);
+    const int vr = 4 * g + (i16 >> 2);                   // tokens vr and vr + 16 share a swizzle
+    const int zv = (vr >> 1) & 7;
+    const int bit = (i16 >> 1) & 1;
 #pragma unroll
-    for (int rb = 0; rb < RB; rb++) s[rb][tb] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
-    const int r = 16 * tb + i16;
-    const int rsw = (r >> 1) & 7;
-#pragma unroll
-    for (int k = 0; k < kQSteps; k++) {
-      const int c = 4 * k + g;               // 16-byte chunk holding dims 32k + 8g .. +8
-      const int off = r * kRowBytes + (((c & ~7) | ((c & 7) ^ rsw)) << 4);
-      const bf16x8_t kf = *(const bf16x8_t*)(cur + off);
-#pragma unroll
-      for (int rb = 0; rb < RB; rb++)
-        s[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][k], s[rb][tb], 0, 0, 0);
-    }
+    for (int m4 = 0; m4 < 4; m4++) vbase[m4] = vr * kRowBytes + 16 * ((2 * m4 + bit) ^ zv) + 8 * (i16 & 1);
   }
-  // ---- online softmax over the lane's 8 tokens of each of its rows
-  bf16x8_t pf[RB];
+};
+
+// One KV tile for one wave: S^T, online softmax, O^T update.  The LDS reads
+// run kKAhead K fragments / kVAhead V^T fragments (two transposing reads
+// each) ahead of their MFMA so that one wave per SIMD keeps the matrix unit
+// and the LDS pipe busy together.  The depths are what fits the register
+// file next to the Q fragments and O accumulators.
+template <int kKAhead, int kVAhead>
+__device__ __forceinline__ void tile_step(const bf16x8_t (&qf)[kRowBlocksPerWave][kQSteps], RowState& st,
+                                          lds_cchar* cur, const LaneOffsets& lo_, int ts,
+                                          const int (&limit)[kRowBlocksPerWave], float scale_log2) {
+  static_assert(kRowBlocksPerWave == 1, "one 16-row block per wave");
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  lds_cchar* kp[2] = {cur + lo_.kbase[0], cur + lo_.kbase[1]};
+  lds_cchar* vp[4] = {cur + lo_.vbase[0], cur + lo_.vbase[1], cur + lo_.vbase[2], cur + lo_.vbase[3]};
+  auto kread = [&](int s) -> bf16x8_t {
+    const int k = s >> 1, tb = s & 1;
+    return *(__attribute__((address_space(3))) const bf16x8_t*)(kp[k & 1] + 18432 * tb + 128 * (k >> 1));
+  };
+  auto vread = [&](int mb, int second) -> u32x2_t {
+    return __builtin_bit_cast(u32x2_t, lds_read_tr16(vp[mb & 3] + 18432 * second + 128 * (mb >> 2)));
+  };
+  // ---- S^T = K . Q^T: two 16-token blocks, two accumulation chains each
+  bf16x8_t kb[kKAhead];
 #pragma unroll
-  for (int rb = 0; rb < RB; rb++) {
+  for (int s = 0; s < kKAhead; s++) kb[s] = kread(s);
+  f32x4v_t sp[2][2];
+#pragma unroll
+  for (int tb = 0; tb < 2; tb++) sp[tb][0] = sp[tb][1] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kQKSteps; s++) {
+    const bf16x8_t kf = kb[s % kKAhead];
+    if (s + kKAhead < kQKSteps) kb[s % kKAhead] = kread(s + kKAhead);
+    const int k = s >> 1, tb = s & 1;
+    sp[tb][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][k], sp[tb][k & 1], 0, 0, 0);
+  }
+  // V^T reads do not depend on P: start them before the softmax
+  u32x2_t vb[kVAhead][2];
+#pragma unroll
+  for (int m = 0; m < kVAhead; m++) {
+    vb[m][0] = vread(m, 0);
+    vb[m][1] = vread(m, 1);
+  }
+  const f32x4v_t s0 = sp[0][0] + sp[0][1], s1 = sp[1][0] + sp[1][1];
+  // ---- online softmax over the lane's 8 tokens of its row
+  bf16x8_t pf;
+  {
     float x[8];
     float mx = kNegInf;
 #pragma unroll
     for (int e = 0; e < 8; e++) {
       const int t = ts + 16 * (e >> 2) + 4 * g + (e & 3);
-      x[e] = t < limit[rb] ? s[rb][e >> 2][e & 3] * scale_log2 : kNegInf;
+      const float sv = e < 4 ? s0[e & 3] : s1[e & 3];
+      x[e] = t < limit[0] ? sv * scale_log2 : kNegInf;
       mx = fmaxf(mx, x[e]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool need = mx > st.m_run[rb] + kRescaleSlack;
+    const bool need = mx > st.m_run[0] + kRescaleSlack;
     if (__any(need)) {
-      const float m_new = need ? mx : st.m_run[rb];
-      const float alpha = need ? __builtin_amdgcn_exp2f(st.m_run[rb] - m_new) : 1.f;   // m_run = -inf gives 0
-      st.l_run[rb] *= alpha;
+      const float m_new = need ? mx : st.m_run[0];
+      const float alpha = need ? __builtin_amdgcn_exp2f(st.m_run[0] - m_new) : 1.f;   // m_run = -inf gives 0
+      st.l_run[0] *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < kVBlocks; mb++) st.acc[rb][mb] *= alpha;
-      st.m_run[rb] = m_new;
+      for (int mb = 0; mb < kVBlocks; mb++) st.acc[0][mb] *= alpha;
+      st.m_run[0] = m_new;
     }
-    const float m_use = st.m_run[rb] == kNegInf ? 0.f : st.m_run[rb];
+    const float m_use = st.m_run[0] == kNegInf ? 0.f : st.m_run[0];
     float p[8];
     float psum = 0.f;
 #pragma unroll
@@ -251,34 +341,30 @@ __device__ __forceinline__ void tile_step(const bf16x8_t (&qf)[kRowBlocksPerWave
       p[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
       psum += p[e];
     }
-    st.l_run[rb] += psum;
+    st.l_run[0] += psum;
     u32x4_t pk;
 #pragma unroll
     for (int e = 0; e < 4; e++)
       pk[e] = (uint32_t)f32_to_bf16_rne(p[2 * e]) | ((uint32_t)f32_to_bf16_rne(p[2 * e + 1]) << 16);
-    pf[rb] = __builtin_bit_cast(bf16x8_t, pk);
+    pf = __builtin_bit_cast(bf16x8_t, pk);
   }
-  // ---- O^T += V^T . P^T; the A operand (dims x tokens) via transposing reads:
-  // lane i of 16-lane group g reads 4 dims of token 4g + i/4 (+16); the
-  // hardware hands lane i dim i of the group's 4 tokens.
-  const int vr = 4 * g + (i16 >> 2);
+  // ---- O^T += V^T . P^T
 #pragma unroll
   for (int mb = 0; mb < kVBlocks; mb++) {
-    const int c = 2 * mb + ((i16 >> 1) & 1);
-    const int o0 = lds_off(vr, c) + 8 * (i16 & 1);
-    const int o1 = lds_off(vr + 16, c) + 8 * (i16 & 1);
-    const u32x2_t lo = __builtin_bit_cast(u32x2_t, lds_read_tr16(cur + o0));
-    const u32x2_t hi = __builtin_bit_cast(u32x2_t, lds_read_tr16(cur + o1));
+    const u32x2_t lo = vb[mb % kVAhead][0], hi = vb[mb % kVAhead][1];
+    if (mb + kVAhead < kVBlocks) {
+      vb[mb % kVAhead][0] = vread(mb + kVAhead, 0);
+      vb[mb % kVAhead][1] = vread(mb + kVAhead, 1);
+    }
     const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-    for (int rb = 0; rb < RB; rb++)
-      st.acc[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb], st.acc[rb][mb], 0, 0, 0);
+    st.acc[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, st.acc[0][mb], 0, 0, 0);
   }
 }
 
 // One piece: rows [128*rb, 128*rb+128) of request b over tiles [tile0, tile1).
 template <bool FP8>
-__device__ void run_piece(const SplitArgs& a, char* lds, Stage<FP8>& stg, const Piece& pc) {
+__device__ void run_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, const LaneOffsets& lo_,
+                          const Piece& pc) {
   constexpr int RB = kRowBlocksPerWave;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
@@ -319,23 +405,29 @@ __device__ void run_piece(const SplitArgs& a, char* lds, Stage<FP8>& stg, const 
   }
 
   const int nt = pc.tile1 - pc.tile0;
+  PageWindow pw;
+  pw.init(a, b, (pc.tile0 * kTile) / a.P, (tok_end + a.P - 1) / a.P);
   if constexpr (FP8) {
-    stg.load(a, b, pc.tile0 * kTile, tok_end);
+    stg.load(a, pw, b, pc.tile0 * kTile, tok_end);
     stg.store(lds);
-    if (nt > 1) stg.load(a, b, (pc.tile0 + 1) * kTile, tok_end);
+    if (nt > 1) stg.load(a, pw, b, (pc.tile0 + 1) * kTile, tok_end);
     for (int it = 0; it < nt; it++) {
       __syncthreads();
       if (it + 1 < nt) stg.store(lds + ((it + 1) & 1) * kTileBytes);
-      if (it + 2 < nt) stg.load(a, b, (pc.tile0 + it + 2) * kTile, tok_end);
-      tile_step(qf, st, lds + (it & 1) * kTileBytes, (pc.tile0 + it) * kTile, limit, a.scale_log2);
+      if (it + 2 < nt) stg.load(a, pw, b, (pc.tile0 + it + 2) * kTile, tok_end);
+      tile_step<6, 2>(qf, st, lds + (it & 1) * kTileBytes, lo_, (pc.tile0 + it) * kTile, limit, a.scale_log2);
     }
   } else {
-    stg.issue(a, lds, b, pc.tile0 * kTile, tok_end);
+    // tiles it+1 .. it+kTileBufs-1 are in flight while tile it is consumed
+#pragma unroll
+    for (int pf = 0; pf < kTileBufs - 1; pf++)
+      if (pf < nt) stg.issue(a, lds + pf * kTileBytes, pw, b, (pc.tile0 + pf) * kTile, tok_end);
     for (int it = 0; it < nt; it++) {
-      stg.wait();
-      __syncthreads();
-      if (it + 1 < nt) stg.issue(a, lds + ((it + 1) & 1) * kTileBytes, b, (pc.tile0 + it + 1) * kTile, tok_end);
-      tile_step(qf, st, lds + (it & 1) * kTileBytes, (pc.tile0 + it) * kTile, limit, a.scale_log2);
+      stg.wait(min(nt - 1 - it, kTileBufs - 2));
+      __syncthreads();   // tile it is in LDS for every wave; buffer (it-1) % kTileBufs is free
+      const int nx = it + kTileBufs - 1;
+      if (nx < nt) stg.issue(a, lds + (nx % kTileBufs) * kTileBytes, pw, b, (pc.tile0 + nx) * kTile, tok_end);
+      tile_step<8, 4>(qf, st, lds + (it % kTileBufs) * kTileBytes, lo_, (pc.tile0 + it) * kTile, limit, a.scale_log2);
     }
   }
   __syncthreads();   // the next piece's prologue overwrites the tile buffers
@@ -362,9 +454,15 @@ __device__ void run_piece(const SplitArgs& a, char* lds, Stage<FP8>& stg, const 
       }
       if (a.lse != nullptr && g == 0) a.lse[orow_id] = lse_nat;
     } else {
-      float* prow = a.part_o + ((int64_t)pc.slot * kRowsPerBlock + row_in_blk[rb]) * kLatentDim;
+      uint16_t* prow = a.part_o + ((int64_t)pc.slot * kRowsPerBlock + row_in_blk[rb]) * kLatentDim;
 #pragma unroll
-      for (int mb = 0; mb < kVBlocks; mb++) *(f32x4v_t*)(prow + 16 * mb + 4 * g) = st.acc[rb][mb] * inv;
+      for (int mb = 0; mb < kVBlocks; mb++) {
+        const f32x4v_t v = st.acc[rb][mb] * inv;
+        u32x2_t w;
+        w[0] = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        w[1] = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        *(u32x2_t*)(prow + 16 * mb + 4 * g) = w;
+      }
       if (g == 0) a.part_lse[(int64_t)pc.slot * kRowsPerBlock + row_in_blk[rb]] = lse_nat;
     }
   }
@@ -372,14 +470,13 @@ __device__ void run_piece(const SplitArgs& a, char* lds, Stage<FP8>& stg, const 
 
 // Block-wide computation of unit_off[0..B] into LDS (balanced mode).
 template <int NT>
-__device__ void build_unit_offsets(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t nrb,
-                                   int32_t* off) {
+__device__ void build_unit_offsets(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t* off) {
   __shared__ int32_t part[NT];
   const int tid = threadIdx.x;
   const int per = (B + NT - 1) / NT;
   const int b0 = tid * per, b1 = min(B, b0 + per);
   int32_t sum = 0;
-  for (int b = b0; b < b1; b++) sum += nrb * units_of(clamp_len(seq_lens[b], max_seq_len));
+  for (int b = b0; b < b1; b++) sum += units_of(clamp_len(seq_lens[b], max_seq_len));
   part[tid] = sum;
   __syncthreads();
   // inclusive scan of part[] (Hillis-Steele)
@@ -392,7 +489,7 @@ __device__ void build_unit_offsets(const int32_t* seq_lens, int32_t B, int32_t m
   int32_t run = tid == 0 ? 0 : part[tid - 1];
   for (int b = b0; b < b1; b++) {
     off[b] = run;
-    run += nrb * units_of(clamp_len(seq_lens[b], max_seq_len));
+    run += units_of(clamp_len(seq_lens[b], max_seq_len));
   }
   if (tid == NT - 1) off[B] = part[NT - 1];
   __syncthreads();
@@ -410,98 +507,107 @@ __device__ __forceinline__ int32_t find_request(const int32_t* off, int32_t B, i
 template <bool FP8>
 __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* tiles = smem;
-  int32_t* off = (int32_t*)(smem + 2 * kTileBytes);
-  // Rows a direct load skips keep what is in LDS; start from zeros.
-  for (int i = threadIdx.x; i < 2 * kTileBytes / 16; i += kSplitThreads) ((u32x4_t*)tiles)[i] = u32x4_t{0u, 0u, 0u, 0u};
+  lds_char* tiles = (lds_char*)smem;
+  int32_t* off = (int32_t*)(smem + kTileBufs * kTileBytes);
+  // Tiles a load skips keep what is in LDS; start from zeros.
+  for (int i = threadIdx.x; i < kTileBufs * kTileBytes / 16; i += kSplitThreads)
+    ((__attribute__((address_space(3))) u32x4_t*)tiles)[i] = u32x4_t{0u, 0u, 0u, 0u};
   Stage<FP8> stg;
   stg.init();
-  const int64_t g = blockIdx.x;
+  LaneOffsets lo_;
+  lo_.init();
+  int64_t grp;
+  int32_t rb;
+  group_of_block(blockIdx.x, a.nrb, &grp, &rb);
   if (a.num_splits > 0) {
     __syncthreads();
-    const int64_t blk = g / a.num_splits;
-    const int32_t b = (int32_t)(blk / a.nrb);
+    if (grp >= a.NG) return;
+    const int32_t b = (int32_t)(grp / a.num_splits);
     const int32_t U = units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
     Piece pc;
-    if (forced_piece(g, a.nrb, a.num_splits, U, b, &pc)) run_piece<FP8>(a, tiles, stg, pc);
+    if (forced_piece(grp, rb, a.nrb, a.num_splits, U, &pc)) run_piece<FP8>(a, tiles, stg, lo_, pc);
     return;
   }
-  build_unit_offsets<kSplitThreads>(a.seq_lens, a.B, a.max_seq_len, a.nrb, off);
-  if (g == 0)
+  build_unit_offsets<kSplitThreads>(a.seq_lens, a.B, a.max_seq_len, off);
+  if (blockIdx.x == 0)
     for (int b = threadIdx.x; b <= a.B; b += kSplitThreads) a.unit_off_ws[b] = off[b];
+  if (grp >= a.NG) return;
   auto uo = [&](int32_t b) -> int64_t { return off[b]; };
   auto fr = [&](int64_t u) -> int32_t { return find_request(off, a.B, u); };
-  balanced_pieces(g, a.G, a.nrb, uo, fr, a.B, [&](const Piece& pc) { run_piece<FP8>(a, tiles, stg, pc); });
+  balanced_pieces(grp, a.NG, rb, a.nrb, uo, fr, a.B,
+                  [&](const Piece& pc) { run_piece<FP8>(a, tiles, stg, lo_, pc); });
 }
 
 // ---- combine: merge the partial results of each split row block by LSE
-
-
-constexpr int kCombineRowsPerBlock = 16;
-
-__device__ __forceinline__ int64_t combine_slot(const CombineArgs& a, int64_t blk_first_unit, int64_t g,
-                                                int64_t g0) {
-  const int64_t total = a.unit_off_ws[a.B];
-  return (g == g0 && wg_start(g0, total, a.G) != blk_first_unit) ? 2 * g0 + 1 : 2 * g;
-}
+// One wave per query row: lanes load the pieces' LSEs in parallel, then the
+// 512-wide bf16 partials are summed with weights exp(lse_s - LSE).
+constexpr int kCombineRowsPerBlock = kThreads / 64;
 
 __global__ __launch_bounds__(kThreads) void mla_combine_kernel(CombineArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int chunks = kRowsPerBlock / kCombineRowsPerBlock;
   const int64_t blk = blockIdx.x / chunks;     // b * nrb + rb
-  const int chunk = blockIdx.x - (int)(blk * chunks);
+  const int row_in_blk = (int)(blockIdx.x - blk * chunks) * kCombineRowsPerBlock + wave;
   const int32_t b = (int32_t)(blk / a.nrb), rb = (int32_t)(blk - (int64_t)b * a.nrb);
+  const int row = rb * kRowsPerBlock + row_in_blk;
+  if (row >= a.R) return;
   const int32_t U = units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
-  // the pieces of this row block: workgroups [g0, g1] (balanced) or slots blk*S + s (forced)
+  // the pieces of this row block: groups [g0, g1]
   int64_t g0, g1, first_unit = 0, total = 0;
   if (a.num_splits > 0) {
     const int32_t Sp = a.num_splits < U ? a.num_splits : U;
     if (Sp <= 1) return;
-    g0 = blk * a.num_splits;
+    g0 = (int64_t)b * a.num_splits;
     g1 = g0 + Sp - 1;
   } else {
     total = a.unit_off_ws[a.B];
-    first_unit = a.unit_off_ws[b] + (int64_t)rb * U;
-    g0 = wg_of_unit(first_unit, total, a.G);
-    g1 = wg_of_unit(first_unit + U - 1, total, a.G);
+    first_unit = a.unit_off_ws[b];
+    g0 = wg_of_unit(first_unit, total, a.NG);
+    g1 = wg_of_unit(first_unit + U - 1, total, a.NG);
     if (g0 == g1) return;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = 0; i < kCombineRowsPerBlock / 4; i++) {
-    const int row_in_blk = chunk * kCombineRowsPerBlock + wave * (kCombineRowsPerBlock / 4) + i;
-    const int row = rb * kRowsPerBlock + row_in_blk;
-    if (row >= a.R) break;
-    float M = kNegInf;
-    for (int64_t g = g0; g <= g1; g++) {
-      if (a.num_splits == 0 && wg_start(g, total, a.G) == wg_start(g + 1, total, a.G)) continue;
-      const int64_t slot = a.num_splits > 0 ? g : combine_slot(a, first_unit, g, g0);
-      M = fmaxf(M, a.part_lse[slot * kRowsPerBlock + row_in_blk]);
-    }
-    f32x4_t o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    if (M != kNegInf) {
-      for (int64_t g = g0; g <= g1; g++) {
-        if (a.num_splits == 0 && wg_start(g, total, a.G) == wg_start(g + 1, total, a.G)) continue;
-        const int64_t slot = a.num_splits > 0 ? g : combine_slot(a, first_unit, g, g0);
-        const float ls = a.part_lse[slot * kRowsPerBlock + row_in_blk];
-        const float w = ls == kNegInf ? 0.f : __expf(ls - M);
-        den += w;
-        const f32x4_t* src = (const f32x4_t*)(a.part_o + (slot * kRowsPerBlock + row_in_blk) * kLatentDim);
-        const f32x4_t v0 = src[2 * lane], v1 = src[2 * lane + 1];
-        o0 += w * v0;
-        o1 += w * v1;
+  auto slot_of = [&](int64_t g) -> int64_t {
+    if (a.num_splits > 0) return g * a.nrb + rb;
+    if (wg_start(g, total, a.NG) == wg_start(g + 1, total, a.NG)) return -1;   // an empty group
+    return balanced_slot(g, g0, first_unit, total, a.NG, rb, a.nrb);
+  };
+  const int64_t n = g1 - g0 + 1;
+  // pass 1: maximum LSE over the pieces, 64 pieces per step
+  float M = kNegInf;
+  for (int64_t c0 = 0; c0 < n; c0 += 64) {
+    const int64_t s = c0 + lane < n ? slot_of(g0 + c0 + lane) : -1;
+    const float ls = s >= 0 ? a.part_lse[s * kRowsPerBlock + row_in_blk] : kNegInf;
+    M = fmaxf(M, ls);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
+  // pass 2: weighted sum; lane l owns dims 8l..8l+7
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (M != kNegInf) {
+    for (int64_t i = 0; i < n; i++) {
+      const int64_t s = slot_of(g0 + i);
+      if (s < 0) continue;
+      const float ls = a.part_lse[s * kRowsPerBlock + row_in_blk];
+      const float w = ls == kNegInf ? 0.f : __expf(ls - M);
+      den += w;
+      const u32x4_t v = *(const u32x4_t*)(a.part_o + (s * kRowsPerBlock + row_in_blk) * kLatentDim + 8 * lane);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        o[2 * e] += w * __builtin_bit_cast(float, v[e] << 16);
+        o[2 * e + 1] += w * __builtin_bit_cast(float, v[e] & 0xFFFF0000u);
       }
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    const int32_t jq = row / a.H, h = row - jq * a.H;
-    const int64_t orow = (int64_t)(b * a.q_len + jq) * a.H + h;
-    u32x4_t w;
-    w[0] = (uint32_t)f32_to_bf16_rne(o0[0] * inv) | ((uint32_t)f32_to_bf16_rne(o0[1] * inv) << 16);
-    w[1] = (uint32_t)f32_to_bf16_rne(o0[2] * inv) | ((uint32_t)f32_to_bf16_rne(o0[3] * inv) << 16);
-    w[2] = (uint32_t)f32_to_bf16_rne(o1[0] * inv) | ((uint32_t)f32_to_bf16_rne(o1[1] * inv) << 16);
-    w[3] = (uint32_t)f32_to_bf16_rne(o1[2] * inv) | ((uint32_t)f32_to_bf16_rne(o1[3] * inv) << 16);
-    *(u32x4_t*)(a.out + orow * kLatentDim + 8 * lane) = w;
-    if (a.lse != nullptr && lane == 0) a.lse[orow] = den > 0.f ? M + __logf(den) : kNegInf;
   }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const int32_t jq = row / a.H, h = row - jq * a.H;
+  const int64_t orow = (int64_t)(b * a.q_len + jq) * a.H + h;
+  u32x4_t w;
+#pragma unroll
+  for (int e = 0; e < 4; e++)
+    w[e] = (uint32_t)f32_to_bf16_rne(o[2 * e] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * e + 1] * inv) << 16);
+  *(u32x4_t*)(a.out + orow * kLatentDim + 8 * lane) = w;
+  if (a.lse != nullptr && lane == 0) a.lse[orow] = den > 0.f ? M + __logf(den) : kNegInf;
 }
 
 // ---- debug: gather one request's stored rows through the block table
@@ -524,32 +630,35 @@ __global__ __launch_bounds__(kThreads) void mla_gather_kernel(const void* pool, 
 
 // ---- debug: the plan as the decode kernel computes it
 __global__ __launch_bounds__(kThreads) void mla_plan_kernel(const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
-                                                             int32_t nrb, int32_t num_splits, int64_t G,
+                                                             int32_t nrb, int32_t num_splits, int64_t NG,
                                                              int32_t max_per_wg, int32_t* pieces,
                                                              int32_t* counts) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int32_t* off = (int32_t*)smem;
-  const int64_t g = blockIdx.x;
+  int64_t grp;
+  int32_t rb;
+  group_of_block(blockIdx.x, nrb, &grp, &rb);
+  const int64_t wg = grp * nrb + rb;      // logical workgroup index of the plan
   int32_t n = 0;
   auto emit = [&](const Piece& pc) {
     if (threadIdx.x == 0 && n < max_per_wg) {
-      int32_t* o = pieces + ((int64_t)g * max_per_wg + n) * 6;
-      o[0] = (int32_t)g; o[1] = pc.b; o[2] = pc.rb; o[3] = pc.tile0; o[4] = pc.tile1; o[5] = pc.slot;
+      int32_t* o = pieces + (wg * max_per_wg + n) * 6;
+      o[0] = (int32_t)wg; o[1] = pc.b; o[2] = pc.rb; o[3] = pc.tile0; o[4] = pc.tile1; o[5] = pc.slot;
     }
     n++;
   };
+  if (num_splits == 0) build_unit_offsets<kThreads>(seq_lens, B, max_seq_len, off);
+  if (grp >= NG) return;
   if (num_splits > 0) {
-    const int64_t blk = g / num_splits;
-    const int32_t b = (int32_t)(blk / nrb);
+    const int32_t b = (int32_t)(grp / num_splits);
     Piece pc;
-    if (forced_piece(g, nrb, num_splits, units_of(clamp_len(seq_lens[b], max_seq_len)), b, &pc)) emit(pc);
+    if (forced_piece(grp, rb, nrb, num_splits, units_of(clamp_len(seq_lens[b], max_seq_len)), &pc)) emit(pc);
   } else {
-    build_unit_offsets<kThreads>(seq_lens, B, max_seq_len, nrb, off);
     auto uo = [&](int32_t b) -> int64_t { return off[b]; };
     auto fr = [&](int64_t u) -> int32_t { return find_request(off, B, u); };
-    balanced_pieces(g, G, nrb, uo, fr, B, emit);
+    balanced_pieces(grp, NG, rb, nrb, uo, fr, B, emit);
   }
-  if (threadIdx.x == 0) counts[g] = n;
+  if (threadIdx.x == 0) counts[wg] = n;
 }
 
 }  // namespace mla
@@ -558,7 +667,7 @@ __global__ __launch_bounds__(kThreads) void mla_plan_kernel(const int32_t* seq_l
 extern "C" {
 
 size_t mla_split_lds_bytes(int32_t B, int32_t num_splits) {
-  return 2 * (size_t)mla::kTileBytes + (num_splits > 0 ? 0 : ((size_t)B + 1) * 4);
+  return (size_t)mla::kTileBufs * mla::kTileBytes + (num_splits > 0 ? 0 : ((size_t)B + 1) * 4);
 }
 
 hipError_t mla_launch_split(const mla::SplitArgs* a, int fp8, hipStream_t stream) {
@@ -571,10 +680,11 @@ hipError_t mla_launch_split(const mla::SplitArgs* a, int fp8, hipStream_t stream
     if (e != hipSuccess) return e;
     attr_set[fp8 ? 1 : 0] = true;
   }
+  const unsigned grid = (unsigned)mla::launch_grid(a->NG, a->nrb);
   if (fp8)
-    hipLaunchKernelGGL(mla::mla_split_kernel<true>, dim3((unsigned)a->G), dim3(mla::kSplitThreads), lds, stream, *a);
+    hipLaunchKernelGGL(mla::mla_split_kernel<true>, dim3(grid), dim3(mla::kSplitThreads), lds, stream, *a);
   else
-    hipLaunchKernelGGL(mla::mla_split_kernel<false>, dim3((unsigned)a->G), dim3(mla::kSplitThreads), lds, stream, *a);
+    hipLaunchKernelGGL(mla::mla_split_kernel<false>, dim3(grid), dim3(mla::kSplitThreads), lds, stream, *a);
   return hipGetLastError();
 }
 
@@ -598,10 +708,10 @@ hipError_t mla_launch_gather(const void* pool, const int32_t* bt, const int32_t*
 }
 
 hipError_t mla_launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t nrb, int32_t num_splits,
-                           int64_t G, int32_t max_per_wg, int32_t* pieces, int32_t* counts, hipStream_t stream) {
+                           int64_t NG, int32_t max_per_wg, int32_t* pieces, int32_t* counts, hipStream_t stream) {
   const size_t lds = num_splits > 0 ? 16 : ((size_t)B + 1) * 4;
-  hipLaunchKernelGGL(mla::mla_plan_kernel, dim3((unsigned)G), dim3(mla::kThreads), lds, stream, seq_lens, B,
-                     max_seq_len, nrb, num_splits, G, max_per_wg, pieces, counts);
+  hipLaunchKernelGGL(mla::mla_plan_kernel, dim3((unsigned)mla::launch_grid(NG, nrb)), dim3(mla::kThreads), lds, stream,
+                     seq_lens, B, max_seq_len, nrb, num_splits, NG, max_per_wg, pieces, counts);
   return hipGetLastError();
 }
 

@@ -1,25 +1,28 @@
 // mla_plan.h -- split-KV work planning of libmla, shared by the host mirror
 // and the device kernels so that both produce the same plan.
 //
-// Work unit: one 32-token tile of one request for one block of 64 query
-// rows (rows are (j, h) pairs, j-major, j < q_len, h < H).  A request with L
-// tokens has U = max(1, ceil(L/32)) units per row block (a request with no
-// token still gets one unit, which writes out = 0 and lse = -inf).  Units are
-// ordered (request, row block, tile).
+// Query rows of a request are (j, h) pairs, row = j*H + h, cut into row
+// blocks of 64; a request has nrb = ceil(q_len*H / 64) of them.  One
+// workgroup handles one row block.  The nrb workgroups of a request form a
+// group: they walk the same 32-token KV tiles at the same time, and the
+// launch order puts them on the same XCD (workgroup i runs on XCD i mod 8),
+// so the second read of each tile is served by that XCD's L2.
+//
+// Work unit: one 32-token tile of one request.  A request with L tokens has
+// U = max(1, ceil(L/32)) units (a request with no token still gets one unit,
+// which writes out = 0 and lse = -inf).  Units are ordered (request, tile).
 //
 // Balanced mode (num_splits == 0), in the spirit of the tile-scheduler
 // metadata the pages obtain from get_mla_metadata ("tokenspeed flashmla.py",
-// FlashMLABackend._init_decode_metadata): G workgroups each take a
-// contiguous, equal share [start(g), start(g+1)) of all units, with
-// start(g) = floor(g*total/G).  A share is cut into pieces at row-block
-// boundaries.  A piece that covers its whole row block writes the output;
-// any other piece writes a partial result to slot 2g (the workgroup's first
-// piece) or 2g+1 (its last piece), and the combine merges the partials of a
-// row block from the workgroups that touch it.
+// FlashMLABackend._init_decode_metadata): NG groups each take a contiguous,
+// equal share [start(g), start(g+1)) of all units, start(g) =
+// floor(g*total/NG), cut into pieces at request boundaries.  A piece that
+// covers a whole request writes the output; any other piece writes a partial
+// result to slot 2*wg (the group's first piece) or 2*wg+1 (its last piece),
+// wg = g*nrb + rb, and the combine merges the partials of a row block.
 //
-// Forced mode (num_splits = S > 0): each row block's U tiles are cut into
-// S' = min(S, U) near-equal pieces, one workgroup each; workgroup
-// g = (b*nrb + rb)*S + s, slot g when S' > 1.
+// Forced mode (num_splits = S > 0): group g = b*S + s takes piece s of the
+// S' = min(S, U) near-equal pieces of request b; slot wg when S' > 1.
 #pragma once
 #include <stdint.h>
 
@@ -35,7 +38,8 @@ constexpr int kRowDim = 576;       // latent 512 + rope 64
 constexpr int kLatentDim = 512;
 constexpr int kTile = 32;          // tokens per KV tile
 constexpr int kRowsPerBlock = 64;  // query rows per workgroup (4 waves x 16)
-constexpr int kMaxBatch = 16384;
+constexpr int kMaxBatch = 8192;    // bounded by the LDS that holds the plan next to the KV tiles
+constexpr int kXcds = 8;           // workgroup i is dispatched to XCD i mod 8
 
 MLA_HD int32_t clamp_len(int32_t L, int32_t max_seq_len) {
   return L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
@@ -47,73 +51,89 @@ MLA_HD int32_t units_of(int32_t L) {
 MLA_HD int32_t row_blocks(int32_t q_len, int32_t heads) {
   return (q_len * heads + kRowsPerBlock - 1) / kRowsPerBlock;
 }
-// First unit of workgroup g in balanced mode.
+// First unit of group g in balanced mode.
 MLA_HD int64_t wg_start(int64_t g, int64_t total, int64_t G) { return g * total / G; }
-// The workgroup whose share holds unit u (0 <= u < total): the largest g with start(g) <= u.
+// The group whose share holds unit u (0 <= u < total): the largest g with start(g) <= u.
 MLA_HD int64_t wg_of_unit(int64_t u, int64_t total, int64_t G) { return ((u + 1) * G - 1) / total; }
 
-// Workgroups the decode launches.  ub_units = B * nrb * units_of(max_seq_len)
-// bounds the true unit count, so a balanced grid never exceeds the work.
-MLA_HD int64_t grid_size(int32_t B, int32_t nrb, int32_t max_seq_len, int32_t num_splits, int32_t target) {
+// Groups of the plan.  Balanced: about target workgroups, never more groups
+// than B * units_of(max_seq_len) (which bounds the true unit count).
+MLA_HD int64_t group_count(int32_t B, int32_t nrb, int32_t max_seq_len, int32_t num_splits, int32_t target) {
   if (B <= 0) return 0;
-  if (num_splits > 0) return (int64_t)B * nrb * num_splits;
-  int64_t ub = (int64_t)B * nrb * units_of(max_seq_len);
-  int64_t t = target < 1 ? 1 : target;
+  if (num_splits > 0) return (int64_t)B * num_splits;
+  const int64_t ub = (int64_t)B * units_of(max_seq_len);
+  int64_t t = ((int64_t)(target < 1 ? 1 : target) + nrb - 1) / nrb;
   return ub < t ? ub : t;
 }
+// Workgroups launched: groups padded to a multiple of the XCD count, nrb each.
+MLA_HD int64_t launch_grid(int64_t groups, int32_t nrb) {
+  return (groups + kXcds - 1) / kXcds * kXcds * nrb;
+}
 // Partial-result slots the workspace holds.
-MLA_HD int64_t slot_count(int64_t grid, int32_t num_splits) { return num_splits > 0 ? grid : 2 * grid; }
+MLA_HD int64_t slot_count(int64_t groups, int32_t nrb, int32_t num_splits) {
+  return (num_splits > 0 ? 1 : 2) * groups * nrb;
+}
+// Launch index -> (group, row block): all nrb members of a group share an XCD.
+MLA_HD void group_of_block(int64_t blk, int32_t nrb, int64_t* group, int32_t* rb) {
+  const int64_t xcd = blk % kXcds, q = blk / kXcds;
+  *rb = (int32_t)(q % nrb);
+  *group = (q / nrb) * kXcds + xcd;
+}
 
 struct Piece {
   int32_t b, rb, tile0, tile1, slot;
 };
 
-// Pieces of balanced-mode workgroup g.  unit_off(b) = nrb * sum_{b' < b} U_b'
-// for b in [0, B]; `find(u)` returns the request b with unit_off(b) <= u <
-// unit_off(b+1).  fn(Piece) is called for each piece in order.
+// Pieces of balanced-mode group g for row block rb.  unit_off(b) = sum_{b' <
+// b} U_b' for b in [0, B]; `find(u)` returns the request b with unit_off(b) <=
+// u < unit_off(b+1).  fn(Piece) is called for each piece in order.
 template <class Off, class Find, class Fn>
-MLA_HD void balanced_pieces(int64_t g, int64_t G, int32_t nrb, const Off& unit_off, const Find& find, int32_t B,
-                            Fn&& fn) {
+MLA_HD void balanced_pieces(int64_t g, int64_t G, int32_t rb, int32_t nrb, const Off& unit_off, const Find& find,
+                            int32_t B, Fn&& fn) {
   const int64_t total = unit_off(B);
   const int64_t u_begin = wg_start(g, total, G), u_end = wg_start(g + 1, total, G);
   if (u_begin >= u_end) return;
+  const int64_t wg = g * nrb + rb;
   int32_t b = find(u_begin);
   int64_t u = u_begin;
   while (u < u_end) {
-    const int64_t ob = unit_off(b);
-    const int32_t U = (int32_t)((unit_off(b + 1) - ob) / nrb);
-    const int64_t rel = u - ob;
-    const int32_t rb = (int32_t)(rel / U);
-    const int32_t tile0 = (int32_t)(rel - (int64_t)rb * U);
-    const int64_t blk_end = ob + (int64_t)(rb + 1) * U;
-    const int64_t pe = blk_end < u_end ? blk_end : u_end;
-    const int32_t tile1 = tile0 + (int32_t)(pe - u);
-    const bool whole = tile0 == 0 && tile1 == U;
+    const int64_t ob = unit_off(b), oe = unit_off(b + 1);
+    const int32_t U = (int32_t)(oe - ob);
+    const int64_t pe = oe < u_end ? oe : u_end;
     Piece pc;
     pc.b = b;
     pc.rb = rb;
-    pc.tile0 = tile0;
-    pc.tile1 = tile1;
-    pc.slot = whole ? -1 : (int32_t)(2 * g + (u == u_begin ? 0 : 1));
+    pc.tile0 = (int32_t)(u - ob);
+    pc.tile1 = (int32_t)(pe - ob);
+    const bool whole = pc.tile0 == 0 && pc.tile1 == U;
+    pc.slot = whole ? -1 : (int32_t)(2 * wg + (u == u_begin ? 0 : 1));
     fn(pc);
     u = pe;
-    if (u == unit_off(b + 1)) b++;
+    b++;
   }
 }
 
-// The single piece of forced-mode workgroup g, or false if g has none.
-MLA_HD bool forced_piece(int64_t g, int32_t nrb, int32_t S, int32_t U_of_b_known, int32_t b, Piece* pc) {
-  const int64_t blk = g / S;
-  const int32_t s = (int32_t)(g - blk * S);
-  const int32_t U = U_of_b_known;
+// The single piece of forced-mode group g for row block rb, or false.  U is
+// the unit count of request b = g / S.
+MLA_HD bool forced_piece(int64_t g, int32_t rb, int32_t nrb, int32_t S, int32_t U, Piece* pc) {
+  const int32_t b = (int32_t)(g / S);
+  const int32_t s = (int32_t)(g - (int64_t)b * S);
   const int32_t Sp = S < U ? S : U;
   if (s >= Sp) return false;
   pc->b = b;
-  pc->rb = (int32_t)(blk - (int64_t)b * nrb);
+  pc->rb = rb;
   pc->tile0 = (int32_t)((int64_t)s * U / Sp);
   pc->tile1 = (int32_t)((int64_t)(s + 1) * U / Sp);
-  pc->slot = Sp > 1 ? (int32_t)g : -1;
+  pc->slot = Sp > 1 ? (int32_t)(g * nrb + rb) : -1;
   return true;
+}
+
+// Slot of the piece that group g contributes to row block rb of a request
+// whose units start at first_unit (balanced mode, g in [g0, g1]).
+MLA_HD int64_t balanced_slot(int64_t g, int64_t g0, int64_t first_unit, int64_t total, int64_t G, int32_t rb,
+                             int32_t nrb) {
+  const bool second = g == g0 && wg_start(g0, total, G) != first_unit;
+  return 2 * (g * nrb + rb) + (second ? 1 : 0);
 }
 
 }  // namespace mla

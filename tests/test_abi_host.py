@@ -53,7 +53,7 @@ def test_params_struct_layout():
     (dict(q_len=65), mla.MLA_ERR_NOT_SUPPORTED),
     (dict(num_heads=257), mla.MLA_ERR_NOT_SUPPORTED),
     (dict(q_len=64, num_heads=128), mla.MLA_ERR_NOT_SUPPORTED),   # q_len*H > 4096
-    (dict(batch=16385), mla.MLA_ERR_NOT_SUPPORTED),
+    (dict(batch=8193), mla.MLA_ERR_NOT_SUPPORTED),
     (dict(num_pages=0), mla.MLA_ERR_INVALID_VALUE),
     (dict(max_seq_len=-1), mla.MLA_ERR_INVALID_VALUE),
     (dict(block_table_stride=4), mla.MLA_ERR_INVALID_VALUE),     # 4*64 < 257
@@ -112,17 +112,18 @@ def test_empty_batch_is_a_noop(L):
 
 
 def test_workspace_size_formula():
-    # balanced: grid = min(CUs, B*nrb*units(max)); slots = 2*grid; 64 rows x (512 + 1) floats per slot
-    p = good(batch=64, num_heads=128, max_seq_len=4096, block_table_stride=64, num_cus=256)
-    grid = min(256, 64 * 2 * 128)
-    slots = 2 * grid
+    # balanced: groups = min(ceil(CUs / nrb), B*units(max)); slots = 2 * groups * nrb;
+    # per slot 64 rows x (512 bf16 + 1 fp32 lse)
     a256 = lambda x: (x + 255) // 256 * 256
-    expect = a256(65 * 4) + a256(slots * 64 * 4) + slots * 64 * 512 * 4
+    p = good(batch=64, num_heads=128, max_seq_len=4096, block_table_stride=64, num_cus=256)
+    groups = min(256 // 2, 64 * 128)
+    slots = 2 * groups * 2
+    expect = a256(65 * 4) + a256(slots * 64 * 4) + slots * 64 * 512 * 2
     assert mla.mla_decode_workspace_size(p) == expect
-    # forced splits: grid = B*nrb*S, slots = grid
+    # forced splits: groups = B*S, slots = groups * nrb
     p = good(batch=3, num_heads=128, num_splits=5, num_cus=0)
-    grid = 3 * 2 * 5
-    assert mla.mla_decode_workspace_size(p) == a256(4 * 4) + a256(grid * 64 * 4) + grid * 64 * 512 * 4
+    slots = 3 * 5 * 2
+    assert mla.mla_decode_workspace_size(p) == a256(4 * 4) + a256(slots * 64 * 4) + slots * 64 * 512 * 2
 
 
 def test_check_inputs_host():
