@@ -33,6 +33,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -43,6 +44,24 @@ constexpr int kThreads = 256;                      // combine / gather / plan ke
 #define MLA_ROWBLOCKS_PER_WAVE 1
 #endif
 constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
+#ifndef MLA_KA
+#define MLA_KA 8
+#endif
+#ifndef MLA_VA
+#define MLA_VA 4
+#endif
+#ifndef MLA_SC
+#define MLA_SC 4
+#endif
+#ifndef MLA_F8_KA
+#define MLA_F8_KA 6
+#endif
+#ifndef MLA_F8_VA
+#define MLA_F8_VA 2
+#endif
+#ifndef MLA_F8_SC
+#define MLA_F8_SC 4
+#endif
 constexpr int kRowsPerWave = 16 * kRowBlocksPerWave;
 constexpr int kSplitWaves = kRowsPerBlock / kRowsPerWave;
 constexpr int kSplitThreads = 64 * kSplitWaves;
@@ -51,20 +70,24 @@ constexpr int kRowBytes = kRowDim * 2;             // 1152: one bf16 row in LDS
 constexpr int kTileBytes = kTile * kRowBytes;      // 36864
 constexpr int kChunks = kTile * kRowDim * 2 / 16;  // 2304 16-byte chunks per bf16 tile
 constexpr int kTileLoads = kChunks / 64;           // 36 wave-wide 1 KB loads per tile
-constexpr int kLoadsPerWave = (kTileLoads + kSplitWaves - 1) / kSplitWaves;   // 5
+constexpr int kLoaderWaves = 4;                    // waves 0..3 issue a bf16 tile's loads
+constexpr int kLoadsPerWave = kTileLoads / kLoaderWaves;   // 9
 constexpr int kQSteps = kRowDim / 32;              // 18 k-steps of 32 over the 576 dims
 constexpr int kVBlocks = kLatentDim / 16;          // 32 blocks of 16 latent dims
 constexpr int kFp8Chunks = kTile * kRowDim / 8;    // 2304 8-byte chunks per fp8 tile
 constexpr int kFp8PerThread = (kFp8Chunks + kSplitThreads - 1) / kSplitThreads;   // 5
 constexpr float kNegInf = -__builtin_inff();
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
+// maxima (vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr float kLn2 = 0.6931471805599453f;
 // A row's running maximum is raised only when a tile's maximum exceeds it by
 // more than this (log2 units); exponentials stay <= 2^8, exact math unchanged.
 constexpr float kRescaleSlack = 8.0f;
 
 static_assert(kChunks % 64 == 0, "tile must be a whole number of wave-wide loads");
-static_assert(kTileLoads % kSplitWaves == 0, "every wave issues the same number of tile loads");
-static_assert(kLoadsPerWave == 9, "the vmcnt immediates in Stage<false>::wait assume 9 loads per wave and tile");
+static_assert(kTileLoads % kLoaderWaves == 0 && kLoaderWaves <= kSplitWaves,
+              "every loader wave issues the same number of tile loads");
 // KV tile buffers in LDS: kTileBufs - 1 tiles are in flight while one is consumed.
 constexpr int kTileBufs = 3;
 static_assert(kTile == 32, "the MFMA layout below assumes 32-token tiles");
@@ -83,6 +106,28 @@ __device__ __forceinline__ int lds_off(int r, int c) {
   return r * kRowBytes + (((c & ~7) | ((c & 7) ^ ((r >> 1) & 7))) << 4);
 }
 
+// Workgroup barrier ordering LDS only.  The tile loop's waves exchange data
+// through LDS alone (tile loads are awaited explicitly with vmcnt before the
+// barrier), so the barrier must not wait for the global loads in flight: a
+// full __syncthreads would drain the tile prefetches at every tile.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One wave-wide 16-byte-per-lane load from global memory straight into LDS:
+// lane l's 16 bytes at gbase + voff land at LDS address lds_addr + 16*l.
+// Issued from asm so that the compiler does not see an LDS write in flight:
+// it would otherwise wait for every outstanding global load before each
+// transposing LDS read.  The caller orders the data with an explicit vmcnt
+// wait and an LDS barrier.  M0 is written here; no compiler-generated code in
+// the tile loop keeps a value in M0.
+__device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2" ::"v"(voff), "s"(lds_addr), "s"(gbase)
+               : "memory");
+}
+
 // Address of the first element of token t of request b, or null when the
 // block-table entry for t is outside [0, N).  The same addressing serves the
 // decode and the debug gather.
@@ -97,14 +142,24 @@ __device__ __forceinline__ const char* token_row(const void* pool, const int32_t
 // (lane l holds entry first + l), so a tile's page id is a lane read rather
 // than a memory load whose wait would also drain the tile loads in flight.
 // Only entries of pages the piece reads are loaded.
+// The window is loaded from asm with its own vmcnt(0): a compiler-visible
+// load here would make the compiler wait for every global load in flight
+// (the tile prefetches included) before each tile's page lookup.  Lanes past
+// the piece's last entry load that last entry again, so every address read is
+// one the piece uses.
 struct PageWindow {
   int32_t vec = -1;
   int32_t first = 0;
   int32_t end = 0;     // one past the last entry the piece reads
   __device__ __forceinline__ void load(const SplitArgs& a, int b, int first_entry) {
     first = first_entry;
+    if (first >= end) {
+      vec = -1;
+      return;
+    }
     const int lane = threadIdx.x & 63;
-    vec = first + lane < end ? a.bt[(int64_t)b * a.W + first + lane] : -1;
+    const int32_t* ptr = a.bt + (int64_t)b * a.W + min(first + lane, end - 1);
+    asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(vec) : "v"(ptr) : "memory");
   }
   __device__ __forceinline__ void init(const SplitArgs& a, int b, int first_entry, int end_entry) {
     end = end_entry;
@@ -131,43 +186,50 @@ struct Stage;
 
 template <>
 struct Stage<false> {
-  int src_off[kLoadsPerWave];   // byte offset inside the tile's global run
-  int row[kLoadsPerWave];       // tile row this lane's chunk belongs to
+  uint32_t src_off[kLoadsPerWave];   // byte offset inside the tile's global run
+  __device__ __forceinline__ static int chunk_row(int i) {   // tile row of this lane's chunk of load i
+    const int p = ((threadIdx.x >> 6) + kLoaderWaves * i) * 64 + (threadIdx.x & 63);
+    return p / 72;
+  }
   __device__ __forceinline__ void init() {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; i++) {
-      const int blk = wave + kSplitWaves * i;
-      const int p = blk * 64 + lane;                 // physical 16-byte chunk of the tile in LDS
+      const int p = (wave + kLoaderWaves * i) * 64 + lane;   // physical 16-byte chunk of the tile in LDS
       const int r = p / 72, pc = p - r * 72;
       const int c = (pc & ~7) | ((pc & 7) ^ ((r >> 1) & 7));   // logical chunk stored there
-      src_off[i] = r * kRowBytes + c * 16;
-      row[i] = r;
+      src_off[i] = (uint32_t)(r * kRowBytes + c * 16);
     }
   }
-  // Issues exactly kLoadsPerWave loads per wave for a tile that holds at
-  // least one valid token (the waits below count on it); rows past the last
-  // valid token re-read the tile's first row, so every LDS row stays finite.
-  // A tile with no valid token (only a request with no token at all) or a
-  // block-table entry outside [0, N) issues nothing.
+  // Issues exactly kLoadsPerWave loads per loader wave for a tile that holds
+  // at least one valid token (the waits below count on it); rows past the
+  // last valid token re-read the tile's first row, so every LDS row stays
+  // finite.  A tile with no valid token (only a request with no token at
+  // all) or a block-table entry outside [0, N) issues nothing.
   __device__ __forceinline__ void issue(const SplitArgs& a, lds_char* buf, PageWindow& pw, int b, int ts,
                                         int tok_end) const {
-    if (ts >= tok_end) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wave >= kLoaderWaves || ts >= tok_end) return;
     const int32_t page = pw.page(a, b, ts / a.P);
     if ((uint32_t)page >= (uint32_t)a.N) return;
     const char* base = (const char*)a.pool + ((int64_t)page * a.P + (ts % a.P)) * (int64_t)kRowBytes;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const bool full = ts + kTile <= tok_end;
+    const uint32_t dst = (uint32_t)(uintptr_t)(buf + wave * 1024);
+    if (ts + kTile <= tok_end) {
+      // whole tile: uniform base + loop-invariant lane offsets
 #pragma unroll
-    for (int i = 0; i < kLoadsPerWave; i++) {
-      lds_char* dst = buf + (wave + kSplitWaves * i) * 1024;
-      const int off = full || ts + row[i] < tok_end ? src_off[i] : src_off[i] - row[i] * kRowBytes;
-      __builtin_amdgcn_global_load_lds((const void*)(base + off), (__attribute__((address_space(3))) void*)dst, 16,
-                                       0, 0);
+      for (int i = 0; i < kLoadsPerWave; i++) dma16(base, src_off[i], dst + kLoaderWaves * 1024 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLoadsPerWave; i++) {
+        const int r = chunk_row(i);
+        const uint32_t off = ts + r < tok_end ? src_off[i] : src_off[i] - (uint32_t)(r * kRowBytes);
+        dma16(base, off, dst + kLoaderWaves * 1024 * i);
+      }
     }
   }
   // Wait until at most `later` tiles' loads (issued after this tile's) are in flight.
   __device__ __forceinline__ void wait(int later) const {
+    static_assert(kLoadsPerWave == 9, "the vmcnt immediates assume 9 loads per loader wave and tile");
     if (later >= 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
     else if (later == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -222,6 +284,50 @@ struct Stage<true> {
   }
 };
 
+// An LDS address the optimiser cannot look into: per-read constant offsets
+// then fold into the DS instructions instead of being re-added to the tile
+// buffer arithmetic for every read.
+__device__ __forceinline__ lds_cchar* opaque_lds(lds_cchar* p) {
+  uint32_t v = (uint32_t)(uintptr_t)p;
+  asm("" : "+v"(v));
+  return (lds_cchar*)(uintptr_t)v;
+}
+
+#ifndef MLA_PIN_ORDER
+#define MLA_PIN_ORDER 1
+#endif
+#ifndef MLA_ACC_IN_AGPR
+#define MLA_ACC_IN_AGPR 0
+#endif
+// O *= alpha for one row block's accumulators.  With MLA_ACC_IN_AGPR the
+// accumulators live in AGPRs (the only way 32 rows of O and Q fit one wave):
+// each element is read, scaled and written back inside one asm statement
+// whose AGPR constraint keeps the register allocator from moving O into
+// VGPRs.  The s_nop guards cover the MFMA-result and AGPR-write hazards the
+// compiler cannot see inside the asm; this path runs only when a row's
+// running maximum grows, so they cost nothing in the steady state.
+__device__ __forceinline__ void rescale_acc(f32x4v_t (&acc)[kVBlocks], float alpha) {
+#if MLA_ACC_IN_AGPR
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int mb = 0; mb < kVBlocks; mb++) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      float x = acc[mb][e];
+      float t;
+      asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                   : "+a"(x), "=&v"(t)
+                   : "v"(alpha));
+      acc[mb][e] = x;
+    }
+  }
+  asm volatile("s_nop 7" ::: "memory");
+#else
+#pragma unroll
+  for (int mb = 0; mb < kVBlocks; mb++) acc[mb] *= alpha;
+#endif
+}
+
 __device__ __forceinline__ s16x4_t lds_read_tr16(lds_cchar* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
 }
@@ -229,8 +335,6 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(lds_cchar* p) {
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
-
-typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 
 // Per-wave running state: kRowBlocksPerWave blocks of 16 rows, lane l owns
 // row l%16 of each block.
@@ -267,20 +371,26 @@ struct LaneOffsets {
   }
 };
 
-// One KV tile for one wave: S^T, online softmax, O^T update.  The LDS reads
-// run kKAhead K fragments / kVAhead V^T fragments (two transposing reads
-// each) ahead of their MFMA so that one wave per SIMD keeps the matrix unit
-// and the LDS pipe busy together.  The depths are what fits the register
-// file next to the Q fragments and O accumulators.
-template <int kKAhead, int kVAhead>
+// One KV tile for one wave: S^T, online softmax, O^T update for each of the
+// wave's RB row blocks.  Every K fragment and V^T fragment read from LDS
+// feeds the MFMAs of all RB blocks.  The LDS reads run kKAhead K fragments /
+// kVAhead V^T fragments (two transposing reads each) ahead of their MFMA so
+// that the matrix unit and the LDS pipe stay busy together; the depths are
+// what fits the register file next to the Q fragments and O accumulators.
+template <int kKAhead, int kVAhead, int kSChains>
 __device__ __forceinline__ void tile_step(const bf16x8_t (&qf)[kRowBlocksPerWave][kQSteps], RowState& st,
                                           lds_cchar* cur, const LaneOffsets& lo_, int ts,
-                                          const int (&limit)[kRowBlocksPerWave], float scale_log2) {
-  static_assert(kRowBlocksPerWave == 1, "one 16-row block per wave");
+                                          const int (&limit)[kRowBlocksPerWave], int lim_min, float scale_log2) {
+  constexpr int RB = kRowBlocksPerWave;
+  static_assert(kSChains == 2 || kSChains == 4, "one or two accumulation chains per token block");
+  constexpr int kCh = kSChains / 2;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
-  lds_cchar* kp[2] = {cur + lo_.kbase[0], cur + lo_.kbase[1]};
-  lds_cchar* vp[4] = {cur + lo_.vbase[0], cur + lo_.vbase[1], cur + lo_.vbase[2], cur + lo_.vbase[3]};
+  lds_cchar* kp[2] = {opaque_lds(cur + lo_.kbase[0]), opaque_lds(cur + lo_.kbase[1])};
+  lds_cchar* vp[4] = {opaque_lds(cur + lo_.vbase[0]), opaque_lds(cur + lo_.vbase[1]),
+                      opaque_lds(cur + lo_.vbase[2]), opaque_lds(cur + lo_.vbase[3])};
+  // every token of the tile is visible to every row of the wave: no mask
+  const bool masked = ts + kTile > lim_min;
   auto kread = [&](int s) -> bf16x8_t {
     const int k = s >> 1, tb = s & 1;
     return *(__attribute__((address_space(3))) const bf16x8_t*)(kp[k & 1] + 18432 * tb + 128 * (k >> 1));
@@ -288,19 +398,28 @@ __device__ __forceinline__ void tile_step(const bf16x8_t (&qf)[kRowBlocksPerWave
   auto vread = [&](int mb, int second) -> u32x2_t {
     return __builtin_bit_cast(u32x2_t, lds_read_tr16(vp[mb & 3] + 18432 * second + 128 * (mb >> 2)));
   };
-  // ---- S^T = K . Q^T: two 16-token blocks, two accumulation chains each
+  // ---- S^T = K . Q^T: two 16-token blocks, kCh accumulation chains each
   bf16x8_t kb[kKAhead];
 #pragma unroll
   for (int s = 0; s < kKAhead; s++) kb[s] = kread(s);
-  f32x4v_t sp[2][2];
+  f32x4v_t sp[RB][2][kCh];
 #pragma unroll
-  for (int tb = 0; tb < 2; tb++) sp[tb][0] = sp[tb][1] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+    for (int tb = 0; tb < 2; tb++)
+#pragma unroll
+      for (int c = 0; c < kCh; c++) sp[rb][tb][c] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kQKSteps; s++) {
     const bf16x8_t kf = kb[s % kKAhead];
     if (s + kKAhead < kQKSteps) kb[s % kKAhead] = kread(s + kKAhead);
     const int k = s >> 1, tb = s & 1;
-    sp[tb][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][k], sp[tb][k & 1], 0, 0, 0);
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++)
+      sp[rb][tb][k % kCh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][k], sp[rb][tb][k % kCh], 0, 0, 0);
+    // keep each step's read kKAhead steps ahead of its MFMA: left alone, the
+    // scheduler sinks the reads next to their use and exposes the LDS latency
+    if (MLA_PIN_ORDER) __builtin_amdgcn_sched_barrier(0);
   }
   // V^T reads do not depend on P: start them before the softmax
   u32x2_t vb[kVAhead][2];
@@ -309,44 +428,52 @@ __device__ __forceinline__ void tile_step(const bf16x8_t (&qf)[kRowBlocksPerWave
     vb[m][0] = vread(m, 0);
     vb[m][1] = vread(m, 1);
   }
-  const f32x4v_t s0 = sp[0][0] + sp[0][1], s1 = sp[1][0] + sp[1][1];
-  // ---- online softmax over the lane's 8 tokens of its row
-  bf16x8_t pf;
-  {
+  // ---- online softmax over the lane's 8 tokens of its row, per row block
+  bf16x8_t pf[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++) {
+    f32x4v_t s0 = sp[rb][0][0], s1 = sp[rb][1][0];
+    if constexpr (kCh == 2) {
+      s0 += sp[rb][0][1];
+      s1 += sp[rb][1][1];
+    }
     float x[8];
+    if (!masked) {
+#pragma unroll
+      for (int e = 0; e < 8; e++) x[e] = (e < 4 ? s0[e & 3] : s1[e & 3]) * scale_log2;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const int t = ts + 16 * (e >> 2) + 4 * g + (e & 3);
+        const float sv = e < 4 ? s0[e & 3] : s1[e & 3];
+        x[e] = t < limit[rb] ? sv * scale_log2 : kNegInf;
+      }
+    }
     float mx = kNegInf;
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-      const int t = ts + 16 * (e >> 2) + 4 * g + (e & 3);
-      const float sv = e < 4 ? s0[e & 3] : s1[e & 3];
-      x[e] = t < limit[0] ? sv * scale_log2 : kNegInf;
-      mx = fmaxf(mx, x[e]);
-    }
+    for (int e = 0; e < 8; e++) mx = fmaxf(mx, x[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool need = mx > st.m_run[0] + kRescaleSlack;
+    const bool need = mx > st.m_run[rb] + kRescaleSlack;
     if (__any(need)) {
-      const float m_new = need ? mx : st.m_run[0];
-      const float alpha = need ? __builtin_amdgcn_exp2f(st.m_run[0] - m_new) : 1.f;   // m_run = -inf gives 0
-      st.l_run[0] *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < kVBlocks; mb++) st.acc[0][mb] *= alpha;
-      st.m_run[0] = m_new;
+      const float m_new = need ? mx : st.m_run[rb];
+      const float alpha = need ? __builtin_amdgcn_exp2f(st.m_run[rb] - m_new) : 1.f;   // m_run = -inf gives 0
+      st.l_run[rb] *= alpha;
+      rescale_acc(st.acc[rb], alpha);
+      st.m_run[rb] = m_new;
     }
-    const float m_use = st.m_run[0] == kNegInf ? 0.f : st.m_run[0];
-    float p[8];
+    const float m_use = st.m_run[rb] == kNegInf ? 0.f : st.m_run[rb];
     float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-      p[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
-      psum += p[e];
-    }
-    st.l_run[0] += psum;
     u32x4_t pk;
 #pragma unroll
-    for (int e = 0; e < 4; e++)
-      pk[e] = (uint32_t)f32_to_bf16_rne(p[2 * e]) | ((uint32_t)f32_to_bf16_rne(p[2 * e + 1]) << 16);
-    pf = __builtin_bit_cast(bf16x8_t, pk);
+    for (int e = 0; e < 4; e++) {
+      const float p0 = __builtin_amdgcn_exp2f(x[2 * e] - m_use);
+      const float p1 = __builtin_amdgcn_exp2f(x[2 * e + 1] - m_use);
+      psum += p0 + p1;
+      pk[e] = (uint32_t)f32_to_bf16_rne(p0) | ((uint32_t)f32_to_bf16_rne(p1) << 16);
+    }
+    st.l_run[rb] += psum;
+    pf[rb] = __builtin_bit_cast(bf16x8_t, pk);
   }
   // ---- O^T += V^T . P^T
 #pragma unroll
@@ -357,7 +484,10 @@ __device__ __forceinline__ void tile_step(const bf16x8_t (&qf)[kRowBlocksPerWave
       vb[mb % kVAhead][1] = vread(mb + kVAhead, 1);
     }
     const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-    st.acc[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, st.acc[0][mb], 0, 0, 0);
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++)
+      st.acc[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb], st.acc[rb][mb], 0, 0, 0);
+    if (MLA_PIN_ORDER) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -382,6 +512,13 @@ __device__ void run_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, co
     hrow[rb] = row_ok[rb] ? row - jrow[rb] * a.H : 0;
     limit[rb] = min(tok_end, L - a.q_len + 1 + jrow[rb]);   // tokens t < limit are visible to this row
   }
+  // smallest limit over the wave's rows: tiles below it need no mask
+  int lim_min = limit[0];
+#pragma unroll
+  for (int rb = 1; rb < RB; rb++) lim_min = min(lim_min, limit[rb]);
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, d));
+  lim_min = __builtin_amdgcn_readfirstlane(lim_min);
 
   // Q^T B-operand fragments: lane holds row i16 of each block, dims 32k + 8g .. +8.
   bf16x8_t qf[RB][kQSteps];
@@ -395,6 +532,10 @@ __device__ void run_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, co
       qf[rb][k] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
+  // Wait for the Q loads here, with a wait the compiler accounts for: left
+  // pending into the tile loop they would make it wait for every global load
+  // in flight (the tile prefetches) at the first MFMA of every tile.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   RowState st;
 #pragma unroll
   for (int rb = 0; rb < RB; rb++) {
@@ -412,25 +553,32 @@ __device__ void run_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, co
     stg.store(lds);
     if (nt > 1) stg.load(a, pw, b, (pc.tile0 + 1) * kTile, tok_end);
     for (int it = 0; it < nt; it++) {
-      __syncthreads();
+      lds_barrier();
       if (it + 1 < nt) stg.store(lds + ((it + 1) & 1) * kTileBytes);
       if (it + 2 < nt) stg.load(a, pw, b, (pc.tile0 + it + 2) * kTile, tok_end);
-      tile_step<6, 2>(qf, st, lds + (it & 1) * kTileBytes, lo_, (pc.tile0 + it) * kTile, limit, a.scale_log2);
+      tile_step<MLA_F8_KA, MLA_F8_VA, MLA_F8_SC>(qf, st, lds + (it & 1) * kTileBytes, lo_, (pc.tile0 + it) * kTile,
+                                                 limit, lim_min, a.scale_log2);
     }
   } else {
     // tiles it+1 .. it+kTileBufs-1 are in flight while tile it is consumed
 #pragma unroll
     for (int pf = 0; pf < kTileBufs - 1; pf++)
       if (pf < nt) stg.issue(a, lds + pf * kTileBytes, pw, b, (pc.tile0 + pf) * kTile, tok_end);
+    int cur_buf = 0, nx_buf = kTileBufs - 1;   // buffers of tile it and of tile it + kTileBufs - 1
     for (int it = 0; it < nt; it++) {
       stg.wait(min(nt - 1 - it, kTileBufs - 2));
-      __syncthreads();   // tile it is in LDS for every wave; buffer (it-1) % kTileBufs is free
+      lds_barrier();   // tile it is in LDS for every wave; the buffer of tile it-1 is free
       const int nx = it + kTileBufs - 1;
-      if (nx < nt) stg.issue(a, lds + (nx % kTileBufs) * kTileBytes, pw, b, (pc.tile0 + nx) * kTile, tok_end);
-      tile_step<8, 4>(qf, st, lds + (it % kTileBufs) * kTileBytes, lo_, (pc.tile0 + it) * kTile, limit, a.scale_log2);
+      if (nx < nt) stg.issue(a, lds + nx_buf * kTileBytes, pw, b, (pc.tile0 + nx) * kTile, tok_end);
+      tile_step<MLA_KA, MLA_VA, MLA_SC>(qf, st, lds + cur_buf * kTileBytes, lo_, (pc.tile0 + it) * kTile, limit,
+                                        lim_min, a.scale_log2);
+      cur_buf = cur_buf == kTileBufs - 1 ? 0 : cur_buf + 1;
+      nx_buf = nx_buf == kTileBufs - 1 ? 0 : nx_buf + 1;
     }
   }
-  __syncthreads();   // the next piece's prologue overwrites the tile buffers
+  // the next piece's prologue overwrites the tile buffers; the loads of this
+  // piece have all been waited for (vmcnt 0 before its last tile)
+  lds_barrier();
 
   // ---- epilogue: each row's denominator is spread over the 4 lane groups
 #pragma unroll

@@ -113,17 +113,20 @@ def test_empty_batch_is_a_noop(L):
 
 def test_workspace_size_formula():
     # balanced: groups = min(ceil(CUs / nrb), B*units(max)); slots = 2 * groups * nrb;
-    # per slot 64 rows x (512 bf16 + 1 fp32 lse)
+    # per slot ROWS_PER_BLOCK rows x (512 bf16 + 1 fp32 lse)
     a256 = lambda x: (x + 255) // 256 * 256
-    p = good(batch=64, num_heads=128, max_seq_len=4096, block_table_stride=64, num_cus=256)
-    groups = min(256 // 2, 64 * 128)
-    slots = 2 * groups * 2
-    expect = a256(65 * 4) + a256(slots * 64 * 4) + slots * 64 * 512 * 2
-    assert mla.mla_decode_workspace_size(p) == expect
+    R = mla.ROWS_PER_BLOCK
+    for heads, q_len in [(128, 1), (128, 4), (16, 1), (64, 3)]:
+        p = good(batch=64, num_heads=heads, q_len=q_len, max_seq_len=4096, block_table_stride=64, num_cus=256)
+        nrb = -(-q_len * heads // R)
+        groups = min(-(-256 // nrb), 64 * 128)
+        slots = 2 * groups * nrb
+        expect = a256(65 * 4) + a256(slots * R * 4) + slots * R * 512 * 2
+        assert mla.mla_decode_workspace_size(p) == expect, (heads, q_len)
     # forced splits: groups = B*S, slots = groups * nrb
-    p = good(batch=3, num_heads=128, num_splits=5, num_cus=0)
-    slots = 3 * 5 * 2
-    assert mla.mla_decode_workspace_size(p) == a256(4 * 4) + a256(slots * 64 * 4) + slots * 64 * 512 * 2
+    p = good(batch=3, num_heads=128, q_len=2, num_splits=5, num_cus=0)
+    slots = 3 * 5 * -(-2 * 128 // R)
+    assert mla.mla_decode_workspace_size(p) == a256(4 * 4) + a256(slots * R * 4) + slots * R * 512 * 2
 
 
 def test_check_inputs_host():

@@ -67,7 +67,8 @@ def test_forced_plan(S):
     L = np.array([0, 1, 31, 32, 33, 300, 4096], dtype=np.int32)
     p = params(len(L), 1, 128, 4096, num_splits=S)
     pieces, grid = mla.mla_plan_host(p, L)
-    assert grid == len(L) * 2 * S
+    nrb = -(-128 // mla.ROWS_PER_BLOCK)
+    assert grid == len(L) * nrb * S
     cover = check_cover(p, L, pieces, grid)
     for (b, rb), lst in cover.items():
         U = max(1, -(-int(L[b]) // 32))
