@@ -57,18 +57,76 @@ class HipEvents:
         self.hip.hipEventDestroy(ctypes.c_void_p(ev))
 
 
-def cpu_baseline(inp, nbytes):
-    """The CPU oracle on the host cores, over the same workload (all requests, all heads)."""
+def cpu_baseline(inp, budget_s: float = 10.0):
+    """The CPU oracle on the host cores over a bounded sample of the same workload:
+    whole requests (all query rows) in batch order until about budget_s seconds
+    of oracle work, at least one request."""
+    import numpy as np
     import oracle
+    import paged_mla_decode_06_amd as mla
     orc = oracle.default()
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-    t0 = time.perf_counter()
-    orc.decode(inp)
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"the whole workload once ({inp.batch} requests x {inp.q_len * inp.heads} query rows, "
-                      f"{int(inp.seq_lens.sum())} cached tokens), fp64 C oracle, OpenMP over query rows"}
+    kv_bytes = 1 if inp.kv_fp8 else 2
+    done, t_total = 0, 0.0
+    while done < inp.batch and (done == 0 or t_total < budget_s):
+        sel = [(done, j, h) for j in range(inp.q_len) for h in range(inp.heads)]
+        t0 = time.perf_counter()
+        orc.decode_rows(inp, sel)
+        t_total += time.perf_counter() - t0
+        done += 1
+    nbytes, _ = mla.algorithmic_work(inp.seq_lens[:done], inp.q_len, inp.heads, inp.page_size, kv_bytes)
+    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": orc.threads(), "kind": "oracle",
+            "seconds": round(t_total, 3),
+            "sample": f"requests 0..{done - 1} of {inp.batch} (all {inp.q_len * inp.heads} query rows each, "
+                      f"{int(np.asarray(inp.seq_lens[:done]).sum())} cached tokens), fp64 C oracle, "
+                      f"OpenMP over query rows; rate = the sample's algorithmic bytes / its time"}
+
+
+def kernel_sources_sha256() -> str:
+    """Hash of the sources the split kernel is built from (counter summaries name it)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_mla_decode_06_amd", "csrc")
+    for name in ("mla_kernels.hip", "mla_plan.h", "mla_args.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    with open(os.path.join(ROOT, "paged_mla_decode_06_amd", "build.py"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per split-kernel launch from the committed counter summary of
+    this workload, or None when there is none or it was taken on other sources."""
+    path = os.path.join(ROOT, "profiles", f"mla_split_kernel.{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain copy kernel of known size (torch's elementwise mul by 1 over float32),
+    run under rocprofv3 --pmc to scale FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n * 4, "bytes_written": n * 4, "reps": reps,
+                                           "kernel": "torch elementwise mul (float32, out=)"}}))
 
 
 def main():
@@ -79,11 +137,18 @@ def main():
     ap.add_argument("--workload", default="deepseek_decode")
     ap.add_argument("--rotate-gib", type=float, default=1.5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain copy kernel of known size (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; the decode runs on one GPU "
               f"(requests shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(1 << 30, 3)
+        return
 
     import numpy as np
     import torch
@@ -139,7 +204,10 @@ def main():
 
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     kv_only = int(inp.seq_lens.astype(np.int64).sum()) * 576 * kv_bytes
-    split_gbs = nbytes / (split_ms * 1e-3) / 1e9
+    # the split kernel's own algorithmic bytes: everything but the output rows
+    # and LSEs, which the combine kernel writes for split requests
+    split_bytes = nbytes - inp.batch * inp.q_len * inp.heads * (512 * 2 + 4)
+    split_gbs = split_bytes / (split_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -165,12 +233,13 @@ def main():
         "event_ms": {"split_kernel": round(split_ms, 5), "combine_kernel": round(comb_ms, 5),
                      "call": round(call_ms, 5)},
         "roofline": {"bound": "hbm", "achieved": round(split_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "mla_split_kernel", "mfma_frac": round(
-                         flops / (split_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
+                     "kernel": "mla_split_kernel", "algorithmic_bytes_per_launch": split_bytes,
+                     "mfma_frac": round(flops / (split_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "path_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, nbytes)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
     print(json.dumps(res))
 
 

@@ -50,6 +50,7 @@ class Oracle:
         self.lib = ctypes.CDLL(libpath)
         L = self.lib
         L.oracle_version.restype = ctypes.c_int
+        L.oracle_threads.restype = ctypes.c_int
         L.oracle_bf16_to_double.restype = ctypes.c_double
         L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_e4m3fn_to_double.restype = ctypes.c_double
@@ -62,6 +63,10 @@ class Oracle:
         L.oracle_merge.restype = None
         L.oracle_merge.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_void_p]
+
+    def threads(self) -> int:
+        """OpenMP threads the oracle's loops use."""
+        return int(self.lib.oracle_threads())
 
     # ---- scalar decoders
     def bf16(self, bits: int) -> float:

@@ -57,6 +57,14 @@ typedef struct {
 
 int oracle_version(void) { return 1 + 1000 * ORACLE_MUTANT; }
 
+/* Threads the OpenMP loops below run on (reported next to CPU timings). */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_threads(void) { return 1; }
+#endif
+
 /* bf16: the upper 16 bits of an IEEE binary32. */
 double oracle_bf16_to_double(uint16_t h) {
   uint32_t u = (uint32_t)h << (MUT(11) ? 15 : 16);

@@ -45,22 +45,22 @@ constexpr int kThreads = 256;                      // combine / gather / plan ke
 #endif
 constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
 #ifndef MLA_KA
-#define MLA_KA 8
+#define MLA_KA 4
 #endif
 #ifndef MLA_VA
-#define MLA_VA 4
+#define MLA_VA 2
 #endif
 #ifndef MLA_SC
-#define MLA_SC 4
+#define MLA_SC 2
 #endif
 #ifndef MLA_F8_KA
-#define MLA_F8_KA 6
+#define MLA_F8_KA 4
 #endif
 #ifndef MLA_F8_VA
 #define MLA_F8_VA 2
 #endif
 #ifndef MLA_F8_SC
-#define MLA_F8_SC 4
+#define MLA_F8_SC 2
 #endif
 constexpr int kRowsPerWave = 16 * kRowBlocksPerWave;
 constexpr int kSplitWaves = kRowsPerBlock / kRowsPerWave;
@@ -77,9 +77,6 @@ constexpr int kVBlocks = kLatentDim / 16;          // 32 blocks of 16 latent dim
 constexpr int kFp8Chunks = kTile * kRowDim / 8;    // 2304 8-byte chunks per fp8 tile
 constexpr int kFp8PerThread = (kFp8Chunks + kSplitThreads - 1) / kSplitThreads;   // 5
 constexpr float kNegInf = -__builtin_inff();
-// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
-// maxima (vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr float kLn2 = 0.6931471805599453f;
 // A row's running maximum is raised only when a tile's maximum exceeds it by
 // more than this (log2 units); exponentials stay <= 2^8, exact math unchanged.
@@ -98,13 +95,59 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) const char lds_cchar;
 
-// Byte offset of logical 16-byte chunk c of LDS row r.  Chunks are XOR-swizzled
-// inside each 128-byte group by bits 1..3 of the row, which, with the
-// 128-byte shift between odd and even rows, puts the same chunk of 16
-// consecutive rows in 16 different 16-byte bank groups.
+// Swizzle of LDS tile row r: the logical 16-byte chunk c of the row is stored
+// at physical chunk c ^ swz(r) (only the low three bits of c change, so a
+// chunk stays inside its 128-byte group).  With the 1152-byte row pitch
+// (odd and even rows half a bank period apart), swz(r) = r mod 8 leaves both
+// reads of the tile free of bank conflicts: the K reads (one chunk of 16
+// consecutive rows per 16 lanes) and the transposing V reads (two adjacent
+// chunks of 4 consecutive rows per 16 lanes); the LDS bank-conflict counter
+// reads zero for the split kernel with it.  swz(r + 16) == swz(r), so the two
+// 16-row halves of a tile share lane offsets.
+__device__ __forceinline__ int swz(int r) { return r & 7; }
+
+// Byte offset of logical 16-byte chunk c of LDS row r.
 __device__ __forceinline__ int lds_off(int r, int c) {
-  return r * kRowBytes + (((c & ~7) | ((c & 7) ^ ((r >> 1) & 7))) << 4);
+  return r * kRowBytes + (((c & ~7) | ((c & 7) ^ swz(r))) << 4);
 }
+
+// The 18 16-byte query fragments of one lane (dims 32k + 8(l/16) .. +8 of its
+// row, k < 18, at byte offsets 64k from p) in one asm statement that also
+// waits for them: nothing the compiler emits can touch the registers before
+// the data is there, and the compiler keeps no record of these loads, so it
+// never waits for them (and for every tile load behind them) inside the tile
+// loop.  The wait covers every vector memory operation issued before, which
+// is why the first tiles' loads are issued before this: their latency then
+// overlaps the query's.
+#define MLA_Q_OUT(k) "=&v"(q[k])
+__device__ __forceinline__ void load_q_fragments(u32x4_t (&q)[18], const void* p) {
+  asm volatile(
+      "global_load_dwordx4 %0, %18, off\n\t"
+      "global_load_dwordx4 %1, %18, off offset:64\n\t"
+      "global_load_dwordx4 %2, %18, off offset:128\n\t"
+      "global_load_dwordx4 %3, %18, off offset:192\n\t"
+      "global_load_dwordx4 %4, %18, off offset:256\n\t"
+      "global_load_dwordx4 %5, %18, off offset:320\n\t"
+      "global_load_dwordx4 %6, %18, off offset:384\n\t"
+      "global_load_dwordx4 %7, %18, off offset:448\n\t"
+      "global_load_dwordx4 %8, %18, off offset:512\n\t"
+      "global_load_dwordx4 %9, %18, off offset:576\n\t"
+      "global_load_dwordx4 %10, %18, off offset:640\n\t"
+      "global_load_dwordx4 %11, %18, off offset:704\n\t"
+      "global_load_dwordx4 %12, %18, off offset:768\n\t"
+      "global_load_dwordx4 %13, %18, off offset:832\n\t"
+      "global_load_dwordx4 %14, %18, off offset:896\n\t"
+      "global_load_dwordx4 %15, %18, off offset:960\n\t"
+      "global_load_dwordx4 %16, %18, off offset:1024\n\t"
+      "global_load_dwordx4 %17, %18, off offset:1088\n\t"
+      "s_waitcnt vmcnt(0)"
+      : MLA_Q_OUT(0), MLA_Q_OUT(1), MLA_Q_OUT(2), MLA_Q_OUT(3), MLA_Q_OUT(4), MLA_Q_OUT(5), MLA_Q_OUT(6),
+        MLA_Q_OUT(7), MLA_Q_OUT(8), MLA_Q_OUT(9), MLA_Q_OUT(10), MLA_Q_OUT(11), MLA_Q_OUT(12), MLA_Q_OUT(13),
+        MLA_Q_OUT(14), MLA_Q_OUT(15), MLA_Q_OUT(16), MLA_Q_OUT(17)
+      : "v"(p)
+      : "memory");
+}
+#undef MLA_Q_OUT
 
 // Workgroup barrier ordering LDS only.  The tile loop's waves exchange data
 // through LDS alone (tile loads are awaited explicitly with vmcnt before the
@@ -186,46 +229,61 @@ struct Stage;
 
 template <>
 struct Stage<false> {
-  uint32_t src_off[kLoadsPerWave];   // byte offset inside the tile's global run
-  __device__ __forceinline__ static int chunk_row(int i) {   // tile row of this lane's chunk of load i
-    const int p = ((threadIdx.x >> 6) + kLoaderWaves * i) * 64 + (threadIdx.x & 63);
-    return p / 72;
-  }
+  // Load i of loader wave w fills the 64 physical LDS chunks starting at
+  // P = 64*(w + kLoaderWaves*i).  The chunk p = P + l of lane l holds logical
+  // chunk (p mod 72) ^ z(r) of row r = p / 72, z(r) = swz(r), so its
+  // source offset inside the tile is 16*(p ^ z(r)) = 16*P + 16*(l ^ z(r))
+  // (P is a multiple of 8 and z only flips the low three bits).  The lane
+  // part 16*(l ^ z) < 1024 takes 10 bits: three loads share a register.
+  static constexpr int kPacked = (kLoadsPerWave + 2) / 3;
+  uint32_t xoff[kPacked];
+  __device__ __forceinline__ static int first_chunk(int wave, int i) { return 64 * (wave + kLoaderWaves * i); }
   __device__ __forceinline__ void init() {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
+    for (int j = 0; j < kPacked; j++) xoff[j] = 0;
+#pragma unroll
     for (int i = 0; i < kLoadsPerWave; i++) {
-      const int p = (wave + kLoaderWaves * i) * 64 + lane;   // physical 16-byte chunk of the tile in LDS
-      const int r = p / 72, pc = p - r * 72;
-      const int c = (pc & ~7) | ((pc & 7) ^ ((r >> 1) & 7));   // logical chunk stored there
-      src_off[i] = (uint32_t)(r * kRowBytes + c * 16);
+      const int r = (first_chunk(wave, i) + lane) / 72;
+      xoff[i / 3] |= (uint32_t)(16 * (lane ^ swz(r))) << (10 * (i % 3));
     }
   }
+  __device__ __forceinline__ uint32_t lane_off(int i) const { return (xoff[i / 3] >> (10 * (i % 3))) & 1023u; }
   // Issues exactly kLoadsPerWave loads per loader wave for a tile that holds
   // at least one valid token (the waits below count on it); rows past the
-  // last valid token re-read the tile's first row, so every LDS row stays
-  // finite.  A tile with no valid token (only a request with no token at
-  // all) or a block-table entry outside [0, N) issues nothing.
-  __device__ __forceinline__ void issue(const SplitArgs& a, lds_char* buf, PageWindow& pw, int b, int ts,
-                                        int tok_end) const {
+  // last valid token re-read the same chunk of the tile's first row, so every
+  // LDS row stays finite.  A tile with no valid token (only a request with no
+  // token at all) or a block-table entry outside [0, N) issues nothing.
+  // Returns the number of loads this wave issued (0 or kLoadsPerWave).
+  __device__ __forceinline__ int issue(const SplitArgs& a, lds_char* buf, PageWindow& pw, int b, int ts,
+                                       int tok_end) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (wave >= kLoaderWaves || ts >= tok_end) return;
+    if (wave >= kLoaderWaves || ts >= tok_end) return 0;
     const int32_t page = pw.page(a, b, ts / a.P);
-    if ((uint32_t)page >= (uint32_t)a.N) return;
+    if ((uint32_t)page >= (uint32_t)a.N) return 0;
     const char* base = (const char*)a.pool + ((int64_t)page * a.P + (ts % a.P)) * (int64_t)kRowBytes;
     const uint32_t dst = (uint32_t)(uintptr_t)(buf + wave * 1024);
-    if (ts + kTile <= tok_end) {
-      // whole tile: uniform base + loop-invariant lane offsets
+    // Opaque copies: the offsets are unpacked here, once per tile, instead of
+    // being hoisted out of the tile loop as nine live registers.
+    Stage<false> o = *this;
 #pragma unroll
-      for (int i = 0; i < kLoadsPerWave; i++) dma16(base, src_off[i], dst + kLoaderWaves * 1024 * i);
+    for (int j = 0; j < kPacked; j++) asm("" : "+v"(o.xoff[j]));
+    if (ts + kTile <= tok_end) {
+      // whole tile: uniform base + 10-bit lane offset
+#pragma unroll
+      for (int i = 0; i < kLoadsPerWave; i++)
+        dma16(base + 16 * first_chunk(wave, i), o.lane_off(i), dst + kLoaderWaves * 1024 * i);
     } else {
+      const int lane = threadIdx.x & 63;
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; i++) {
-        const int r = chunk_row(i);
-        const uint32_t off = ts + r < tok_end ? src_off[i] : src_off[i] - (uint32_t)(r * kRowBytes);
+        const int P = first_chunk(wave, i);
+        const int r = (P + lane) / 72;
+        const uint32_t off = (uint32_t)(16 * P) + o.lane_off(i) - (ts + r < tok_end ? 0u : (uint32_t)(r * kRowBytes));
         dma16(base, off, dst + kLoaderWaves * 1024 * i);
       }
     }
+    return kLoadsPerWave;
   }
   // Wait until at most `later` tiles' loads (issued after this tile's) are in flight.
   __device__ __forceinline__ void wait(int later) const {
@@ -360,11 +418,11 @@ struct LaneOffsets {
   __device__ __forceinline__ void init() {
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, i16 = lane & 15;
-    const int zk = (i16 >> 1) & 7;                       // swizzle of rows i16 and 16 + i16
+    const int zk = swz(i16);                             // swizzle of rows i16 and 16 + i16
 #pragma unroll
     for (int p = 0; p < 2; p++) kbase[p] = i16 * kRowBytes + 16 * ((g + 4 * p) ^ zk);
     const int vr = 4 * g + (i16 >> 2);                   // tokens vr and vr + 16 share a swizzle
-    const int zv = (vr >> 1) & 7;
+    const int zv = swz(vr);
     const int bit = (i16 >> 1) & 1;
 #pragma unroll
     for (int m4 = 0; m4 < 4; m4++) vbase[m4] = vr * kRowBytes + 16 * ((2 * m4 + bit) ^ zv) + 8 * (i16 & 1);
@@ -520,22 +578,6 @@ __device__ void run_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, co
   for (int d = 1; d < 64; d <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, d));
   lim_min = __builtin_amdgcn_readfirstlane(lim_min);
 
-  // Q^T B-operand fragments: lane holds row i16 of each block, dims 32k + 8g .. +8.
-  bf16x8_t qf[RB][kQSteps];
-#pragma unroll
-  for (int rb = 0; rb < RB; rb++) {
-    const uint16_t* qrow = a.q + ((int64_t)(b * a.q_len + jrow[rb]) * a.H + hrow[rb]) * kRowDim + 8 * g;
-#pragma unroll
-    for (int k = 0; k < kQSteps; k++) {
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (row_ok[rb]) x = *(const u32x4_t*)(qrow + 32 * k);
-      qf[rb][k] = __builtin_bit_cast(bf16x8_t, x);
-    }
-  }
-  // Wait for the Q loads here, with a wait the compiler accounts for: left
-  // pending into the tile loop they would make it wait for every global load
-  // in flight (the tile prefetches) at the first MFMA of every tile.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   RowState st;
 #pragma unroll
   for (int rb = 0; rb < RB; rb++) {
@@ -548,6 +590,27 @@ __device__ void run_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, co
   const int nt = pc.tile1 - pc.tile0;
   PageWindow pw;
   pw.init(a, b, (pc.tile0 * kTile) / a.P, (tok_end + a.P - 1) / a.P);
+
+  if constexpr (!FP8) {
+    // tiles it+1 .. it+kTileBufs-1 are in flight while tile it is consumed;
+    // the first of them are issued before the query loads
+#pragma unroll
+    for (int pf = 0; pf < kTileBufs - 1; pf++)
+      if (pf < nt) stg.issue(a, lds + pf * kTileBytes, pw, b, (pc.tile0 + pf) * kTile, tok_end);
+  }
+  // Q^T B-operand fragments: lane holds row i16 of each block, dims 32k + 8g .. +8;
+  // rows past the request's last query row load its first row and are zeroed.
+  static_assert(kQSteps == 18, "load_q_fragments loads 18 fragments");
+  bf16x8_t qf[RB][kQSteps];
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++) {
+    const int64_t qrow_id = row_ok[rb] ? (int64_t)(b * a.q_len + jrow[rb]) * a.H + hrow[rb] : (int64_t)b * a.q_len * a.H;
+    u32x4_t qv[kQSteps];
+    load_q_fragments(qv, a.q + qrow_id * kRowDim + 8 * g);
+#pragma unroll
+    for (int k = 0; k < kQSteps; k++)
+      qf[rb][k] = __builtin_bit_cast(bf16x8_t, row_ok[rb] ? qv[k] : u32x4_t{0u, 0u, 0u, 0u});
+  }
   if constexpr (FP8) {
     stg.load(a, pw, b, pc.tile0 * kTile, tok_end);
     stg.store(lds);
@@ -560,10 +623,6 @@ __device__ void run_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, co
                                                  limit, lim_min, a.scale_log2);
     }
   } else {
-    // tiles it+1 .. it+kTileBufs-1 are in flight while tile it is consumed
-#pragma unroll
-    for (int pf = 0; pf < kTileBufs - 1; pf++)
-      if (pf < nt) stg.issue(a, lds + pf * kTileBytes, pw, b, (pc.tile0 + pf) * kTile, tok_end);
     int cur_buf = 0, nx_buf = kTileBufs - 1;   // buffers of tile it and of tile it + kTileBufs - 1
     for (int it = 0; it < nt; it++) {
       stg.wait(min(nt - 1 - it, kTileBufs - 2));
