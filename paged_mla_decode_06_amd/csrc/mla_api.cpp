@@ -284,8 +284,7 @@ mla_status mla_plan_host(const mla_decode_params* p, const int32_t* seq_lens_hos
     std::vector<int64_t> off((size_t)B + 1, 0);
     for (int32_t b = 0; b < B; b++)
       off[b + 1] = off[b] + mla::units_of(mla::clamp_len(seq_lens_host[b], p->max_seq_len));
-    auto uo = [&](int32_t b) -> int64_t { return off[(size_t)b]; };
-    auto fr = [&](int64_t u) -> int32_t {
+    auto fr = [&](int64_t u) -> int32_t {   // largest b with off[b] <= u
       int32_t lo = 0, hi = B - 1;
       while (lo < hi) {
         const int32_t mid = (lo + hi + 1) >> 1;
@@ -293,9 +292,15 @@ mla_status mla_plan_host(const mla_decode_params* p, const int32_t* seq_lens_hos
       }
       return lo;
     };
-    for (int64_t g = 0; g < NG; g++)
+    auto units = [&](int32_t b) -> int32_t { return mla::units_of(mla::clamp_len(seq_lens_host[b], p->max_seq_len)); };
+    const int64_t total = off[(size_t)B];
+    for (int64_t g = 0; g < NG; g++) {
+      const int64_t u_begin = mla::wg_start(g, total, NG);
+      const int32_t b_first = u_begin < total ? fr(u_begin) : 0;
       for (int32_t rb = 0; rb < nrb; rb++)
-        mla::balanced_pieces(g, NG, rb, nrb, uo, fr, B, [&](const mla::Piece& pc) { emit(pc, g * nrb + rb); });
+        mla::balanced_pieces(g, NG, rb, nrb, total, b_first, off[(size_t)b_first], units,
+                             [&](const mla::Piece& pc) { emit(pc, g * nrb + rb); });
+    }
   }
   *n_pieces = (int32_t)n;
   *grid = (int32_t)lay.wgs;

@@ -48,7 +48,7 @@ constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
 #define MLA_KA 4
 #endif
 #ifndef MLA_VA
-#define MLA_VA 2
+#define MLA_VA 4
 #endif
 #ifndef MLA_SC
 #define MLA_SC 2
@@ -57,25 +57,32 @@ constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
 #define MLA_F8_KA 4
 #endif
 #ifndef MLA_F8_VA
-#define MLA_F8_VA 2
+#define MLA_F8_VA 4
 #endif
 #ifndef MLA_F8_SC
 #define MLA_F8_SC 2
 #endif
 constexpr int kRowsPerWave = 16 * kRowBlocksPerWave;
-constexpr int kSplitWaves = kRowsPerBlock / kRowsPerWave;
+// A split workgroup has kComputeWaves waves that own the query rows and do
+// the MFMA work, and kLoaderWaves waves that only move KV tiles into LDS.
+// A tile load can stall its wave at issue for hundreds of cycles while the
+// memory queue is full; with separate loader waves that stall never holds up
+// a compute wave (each SIMD runs one wave of each kind).
+constexpr int kComputeWaves = kRowsPerBlock / kRowsPerWave;
+constexpr int kLoaderWaves = 4;
+constexpr int kSplitWaves = kComputeWaves + kLoaderWaves;
 constexpr int kSplitThreads = 64 * kSplitWaves;
-static_assert(kSplitWaves * kRowsPerWave == kRowsPerBlock, "waves must tile the row block");
+constexpr int kLoaderThreads = 64 * kLoaderWaves;
+static_assert(kComputeWaves * kRowsPerWave == kRowsPerBlock, "compute waves must tile the row block");
 constexpr int kRowBytes = kRowDim * 2;             // 1152: one bf16 row in LDS
 constexpr int kTileBytes = kTile * kRowBytes;      // 36864
 constexpr int kChunks = kTile * kRowDim * 2 / 16;  // 2304 16-byte chunks per bf16 tile
 constexpr int kTileLoads = kChunks / 64;           // 36 wave-wide 1 KB loads per tile
-constexpr int kLoaderWaves = 4;                    // waves 0..3 issue a bf16 tile's loads
-constexpr int kLoadsPerWave = kTileLoads / kLoaderWaves;   // 9
+constexpr int kLoadsPerWave = kTileLoads / kLoaderWaves;   // 9 per loader wave and tile
 constexpr int kQSteps = kRowDim / 32;              // 18 k-steps of 32 over the 576 dims
 constexpr int kVBlocks = kLatentDim / 16;          // 32 blocks of 16 latent dims
 constexpr int kFp8Chunks = kTile * kRowDim / 8;    // 2304 8-byte chunks per fp8 tile
-constexpr int kFp8PerThread = (kFp8Chunks + kSplitThreads - 1) / kSplitThreads;   // 5
+constexpr int kFp8PerThread = (kFp8Chunks + kLoaderThreads - 1) / kLoaderThreads;   // 9
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.6931471805599453f;
 // A row's running maximum is raised only when a tile's maximum exceeds it by
@@ -83,10 +90,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
 
 static_assert(kChunks % 64 == 0, "tile must be a whole number of wave-wide loads");
-static_assert(kTileLoads % kLoaderWaves == 0 && kLoaderWaves <= kSplitWaves,
-              "every loader wave issues the same number of tile loads");
+static_assert(kTileLoads % kLoaderWaves == 0, "every loader wave issues the same number of tile loads");
 // KV tile buffers in LDS: kTileBufs - 1 tiles are in flight while one is consumed.
-constexpr int kTileBufs = 3;
+constexpr int kTileBufs = 4;
 static_assert(kTile == 32, "the MFMA layout below assumes 32-token tiles");
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -238,13 +244,14 @@ struct Stage<false> {
   static constexpr int kPacked = (kLoadsPerWave + 2) / 3;
   uint32_t xoff[kPacked];
   __device__ __forceinline__ static int first_chunk(int wave, int i) { return 64 * (wave + kLoaderWaves * i); }
-  __device__ __forceinline__ void init() {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // lw: this wave's index among the loader waves
+  __device__ __forceinline__ void init(int lw) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int j = 0; j < kPacked; j++) xoff[j] = 0;
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; i++) {
-      const int r = (first_chunk(wave, i) + lane) / 72;
+      const int r = (first_chunk(lw, i) + lane) / 72;
       xoff[i / 3] |= (uint32_t)(16 * (lane ^ swz(r))) << (10 * (i % 3));
     }
   }
@@ -254,11 +261,11 @@ struct Stage<false> {
   // last valid token re-read the same chunk of the tile's first row, so every
   // LDS row stays finite.  A tile with no valid token (only a request with no
   // token at all) or a block-table entry outside [0, N) issues nothing.
-  // Returns the number of loads this wave issued (0 or kLoadsPerWave).
+  // Called by loader wave lw; returns the number of loads it issued (0 or kLoadsPerWave).
   __device__ __forceinline__ int issue(const SplitArgs& a, lds_char* buf, PageWindow& pw, int b, int ts,
-                                       int tok_end) const {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (wave >= kLoaderWaves || ts >= tok_end) return 0;
+                                       int tok_end, int lw) const {
+    const int wave = lw;
+    if (ts >= tok_end) return 0;
     const int32_t page = pw.page(a, b, ts / a.P);
     if ((uint32_t)page >= (uint32_t)a.N) return 0;
     const char* base = (const char*)a.pool + ((int64_t)page * a.P + (ts % a.P)) * (int64_t)kRowBytes;
@@ -310,8 +317,10 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
 template <>
 struct Stage<true> {
   u32x2_t v[kFp8PerThread];
-  __device__ __forceinline__ void init() {}
+  __device__ __forceinline__ void init(int) {}
+  // Called by the loader waves; lt = thread index among them.
   __device__ __forceinline__ void load(const SplitArgs& a, PageWindow& pw, int b, int ts, int tok_end) {
+    const int lt = threadIdx.x - 64 * kComputeWaves;
     const char* base = nullptr;
     if (ts < tok_end) {
       const int32_t page = pw.page(a, b, ts / a.P);
@@ -319,7 +328,7 @@ struct Stage<true> {
     }
 #pragma unroll
     for (int i = 0; i < kFp8PerThread; i++) {
-      const int ci = threadIdx.x + kSplitThreads * i;
+      const int ci = lt + kLoaderThreads * i;
       const int r = ci / 72, c = ci - r * 72;
       u32x2_t x = {0u, 0u};
       if (base != nullptr && ci < kFp8Chunks && ts + r < tok_end) x = *(const u32x2_t*)(base + r * kRowDim + c * 8);
@@ -327,9 +336,10 @@ struct Stage<true> {
     }
   }
   __device__ __forceinline__ void store(lds_char* buf) const {
+    const int lt = threadIdx.x - 64 * kComputeWaves;
 #pragma unroll
     for (int i = 0; i < kFp8PerThread; i++) {
-      const int ci = threadIdx.x + kSplitThreads * i;
+      const int ci = lt + kLoaderThreads * i;
       if (ci >= kFp8Chunks) continue;
       const int r = ci / 72, c = ci - r * 72;
       u32x4_t y;
@@ -549,12 +559,53 @@ __device__ __forceinline__ void tile_step(const bf16x8_t (&qf)[kRowBlocksPerWave
   }
 }
 
-// One piece: rows [128*rb, 128*rb+128) of request b over tiles [tile0, tile1).
+// The loader waves' side of one piece: the piece's KV tiles into the LDS
+// ring, in step with the compute waves' barriers (one per tile, then the two
+// around the epilogue).
 template <bool FP8>
-__device__ void run_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, const LaneOffsets& lo_,
-                          const Piece& pc) {
+__device__ void load_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, const Piece& pc, int lw) {
+  const int b = pc.b;
+  const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const int tok_end = min(pc.tile1 * kTile, L);
+  const int nt = pc.tile1 - pc.tile0;
+  PageWindow pw;
+  pw.init(a, b, (pc.tile0 * kTile) / a.P, (tok_end + a.P - 1) / a.P);
+  if constexpr (FP8) {
+    // two LDS buffers: tile it+1 is converted in while tile it is consumed,
+    // tile it+2 waits in registers
+    stg.load(a, pw, b, pc.tile0 * kTile, tok_end);
+    stg.store(lds);
+    if (nt > 1) stg.load(a, pw, b, (pc.tile0 + 1) * kTile, tok_end);
+    for (int it = 0; it < nt; it++) {
+      lds_barrier();
+      if (it + 1 < nt) stg.store(lds + ((it + 1) & 1) * kTileBytes);
+      if (it + 2 < nt) stg.load(a, pw, b, (pc.tile0 + it + 2) * kTile, tok_end);
+    }
+  } else {
+    // tiles it+1 .. it+kTileBufs-1 are in flight while tile it is consumed
+#pragma unroll
+    for (int pf = 0; pf < kTileBufs - 1; pf++)
+      if (pf < nt) stg.issue(a, lds + pf * kTileBytes, pw, b, (pc.tile0 + pf) * kTile, tok_end, lw);
+    int nx_buf = kTileBufs - 1;   // buffer of tile it + kTileBufs - 1
+    for (int it = 0; it < nt; it++) {
+      stg.wait(min(nt - 1 - it, kTileBufs - 2));
+      lds_barrier();   // tile it is in LDS for every wave; the buffer of tile it-1 is free
+      const int nx = it + kTileBufs - 1;
+      if (nx < nt) stg.issue(a, lds + nx_buf * kTileBytes, pw, b, (pc.tile0 + nx) * kTile, tok_end, lw);
+      nx_buf = nx_buf == kTileBufs - 1 ? 0 : nx_buf + 1;
+    }
+  }
+  lds_barrier();   // the compute waves are done with the tiles
+  lds_barrier();   // and with the staged output rows
+}
+
+// The compute waves' side of one piece: rows [kRowsPerBlock*rb,
+// kRowsPerBlock*(rb+1)) of request b over tiles [tile0, tile1); writes the
+// piece's output rows (or partial rows) and LSEs.
+template <bool FP8>
+__device__ void compute_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& lo_, const Piece& pc) {
   constexpr int RB = kRowBlocksPerWave;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i16 = lane & 15;
   const int b = pc.b;
   const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
@@ -586,18 +637,8 @@ __device__ void run_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, co
     st.m_run[rb] = kNegInf;
     st.l_run[rb] = 0.f;
   }
-
   const int nt = pc.tile1 - pc.tile0;
-  PageWindow pw;
-  pw.init(a, b, (pc.tile0 * kTile) / a.P, (tok_end + a.P - 1) / a.P);
 
-  if constexpr (!FP8) {
-    // tiles it+1 .. it+kTileBufs-1 are in flight while tile it is consumed;
-    // the first of them are issued before the query loads
-#pragma unroll
-    for (int pf = 0; pf < kTileBufs - 1; pf++)
-      if (pf < nt) stg.issue(a, lds + pf * kTileBytes, pw, b, (pc.tile0 + pf) * kTile, tok_end);
-  }
   // Q^T B-operand fragments: lane holds row i16 of each block, dims 32k + 8g .. +8;
   // rows past the request's last query row load its first row and are zeroed.
   static_assert(kQSteps == 18, "load_q_fragments loads 18 fragments");
@@ -612,34 +653,29 @@ __device__ void run_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, co
       qf[rb][k] = __builtin_bit_cast(bf16x8_t, row_ok[rb] ? qv[k] : u32x4_t{0u, 0u, 0u, 0u});
   }
   if constexpr (FP8) {
-    stg.load(a, pw, b, pc.tile0 * kTile, tok_end);
-    stg.store(lds);
-    if (nt > 1) stg.load(a, pw, b, (pc.tile0 + 1) * kTile, tok_end);
     for (int it = 0; it < nt; it++) {
       lds_barrier();
-      if (it + 1 < nt) stg.store(lds + ((it + 1) & 1) * kTileBytes);
-      if (it + 2 < nt) stg.load(a, pw, b, (pc.tile0 + it + 2) * kTile, tok_end);
       tile_step<MLA_F8_KA, MLA_F8_VA, MLA_F8_SC>(qf, st, lds + (it & 1) * kTileBytes, lo_, (pc.tile0 + it) * kTile,
                                                  limit, lim_min, a.scale_log2);
     }
   } else {
-    int cur_buf = 0, nx_buf = kTileBufs - 1;   // buffers of tile it and of tile it + kTileBufs - 1
+    int cur_buf = 0;   // buffer of tile it
     for (int it = 0; it < nt; it++) {
-      stg.wait(min(nt - 1 - it, kTileBufs - 2));
       lds_barrier();   // tile it is in LDS for every wave; the buffer of tile it-1 is free
-      const int nx = it + kTileBufs - 1;
-      if (nx < nt) stg.issue(a, lds + nx_buf * kTileBytes, pw, b, (pc.tile0 + nx) * kTile, tok_end);
       tile_step<MLA_KA, MLA_VA, MLA_SC>(qf, st, lds + cur_buf * kTileBytes, lo_, (pc.tile0 + it) * kTile, limit,
                                         lim_min, a.scale_log2);
       cur_buf = cur_buf == kTileBufs - 1 ? 0 : cur_buf + 1;
-      nx_buf = nx_buf == kTileBufs - 1 ? 0 : nx_buf + 1;
     }
   }
-  // the next piece's prologue overwrites the tile buffers; the loads of this
-  // piece have all been waited for (vmcnt 0 before its last tile)
+  // the epilogue stages rows in the tile buffers
   lds_barrier();
 
-  // ---- epilogue: each row's denominator is spread over the 4 lane groups
+  // ---- epilogue.  Each row's denominator is spread over the 4 lane groups.
+  // The bf16 rows are staged in LDS (the tile buffers, free after the
+  // barrier above) so that every output row leaves as one contiguous 1 KB
+  // store of a wave instead of 16 rows x 32 bytes per store.
+  constexpr int kStagePitch = kLatentDim * 2 + 16;   // rows 16 bytes apart in the banks
+  static_assert(kRowsPerBlock * kStagePitch <= kTileBufs * kTileBytes, "staged rows fit the tile buffers");
 #pragma unroll
   for (int rb = 0; rb < RB; rb++) {
     float l_tot = st.l_run[rb] + __shfl_xor(st.l_run[rb], 16);
@@ -647,32 +683,40 @@ __device__ void run_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, co
     const bool empty = !(l_tot > 0.f);
     const float inv = empty ? 0.f : a.out_scale / l_tot;
     const float lse_nat = empty ? kNegInf : (st.m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
-    if (!row_ok[rb]) continue;
-    if (pc.slot < 0) {
-      const int64_t orow_id = (int64_t)(b * a.q_len + jrow[rb]) * a.H + hrow[rb];
-      uint16_t* orow = a.out + orow_id * kLatentDim;
+    lds_char* srow = lds + row_in_blk[rb] * kStagePitch + 8 * g;
 #pragma unroll
-      for (int mb = 0; mb < kVBlocks; mb++) {
-        const f32x4v_t v = st.acc[rb][mb] * inv;
-        u32x2_t w;
-        w[0] = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-        w[1] = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-        *(u32x2_t*)(orow + 16 * mb + 4 * g) = w;
+    for (int mb = 0; mb < kVBlocks; mb++) {
+      const f32x4v_t v = st.acc[rb][mb] * inv;
+      u32x2_t w;
+      w[0] = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+      w[1] = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+      *(__attribute__((address_space(3))) u32x2_t*)(srow + 32 * mb) = w;
+    }
+    if (row_ok[rb] && g == 0) {
+      if (pc.slot < 0) {
+        if (a.lse != nullptr) a.lse[(int64_t)(b * a.q_len + jrow[rb]) * a.H + hrow[rb]] = lse_nat;
+      } else {
+        a.part_lse[(int64_t)pc.slot * kRowsPerBlock + row_in_blk[rb]] = lse_nat;
       }
-      if (a.lse != nullptr && g == 0) a.lse[orow_id] = lse_nat;
-    } else {
-      uint16_t* prow = a.part_o + ((int64_t)pc.slot * kRowsPerBlock + row_in_blk[rb]) * kLatentDim;
-#pragma unroll
-      for (int mb = 0; mb < kVBlocks; mb++) {
-        const f32x4v_t v = st.acc[rb][mb] * inv;
-        u32x2_t w;
-        w[0] = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-        w[1] = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-        *(u32x2_t*)(prow + 16 * mb + 4 * g) = w;
-      }
-      if (g == 0) a.part_lse[(int64_t)pc.slot * kRowsPerBlock + row_in_blk[rb]] = lse_nat;
     }
   }
+  // A wave copies out the rows it staged (its own LDS writes are ordered
+  // before its reads): lane l carries bytes 16l .. 16l+15 of the row.
+  for (int rr = 0; rr < kRowsPerWave; rr++) {
+    const int rib = wave * kRowsPerWave + rr;
+    const int row = pc.rb * kRowsPerBlock + rib;
+    if (row >= a.R) break;
+    const u32x4_t v = *(__attribute__((address_space(3))) const u32x4_t*)(lds + rib * kStagePitch + 16 * lane);
+    uint16_t* dst;
+    if (pc.slot < 0) {
+      const int j = row / a.H;
+      dst = a.out + ((int64_t)(b * a.q_len + j) * a.H + (row - j * a.H)) * kLatentDim;
+    } else {
+      dst = a.part_o + ((int64_t)pc.slot * kRowsPerBlock + rib) * kLatentDim;
+    }
+    *(u32x4_t*)(dst + 8 * lane) = v;
+  }
+  lds_barrier();   // every wave has read its rows before the next piece's tile loads land there
 }
 
 // Block-wide computation of unit_off[0..B] into LDS (balanced mode).
@@ -711,38 +755,64 @@ __device__ __forceinline__ int32_t find_request(const int32_t* off, int32_t B, i
   return lo;
 }
 
+// Every wave of a workgroup walks the same pieces: the loader waves fill the
+// tile ring, the compute waves consume it; their barriers pair up one to one.
+template <bool FP8, class PieceFn>
+__device__ __forceinline__ void for_each_piece(const SplitArgs& a, int64_t grp, int32_t rb, int32_t total,
+                                               int32_t b_first, int32_t off_first, PieceFn&& fn) {
+  if (a.num_splits > 0) {
+    const int32_t b = (int32_t)(grp / a.num_splits);
+    const int32_t U = units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
+    Piece pc;
+    if (forced_piece(grp, rb, a.nrb, a.num_splits, U, &pc)) fn(pc);
+    return;
+  }
+  auto units = [&](int32_t b) -> int32_t { return units_of(clamp_len(a.seq_lens[b], a.max_seq_len)); };
+  balanced_pieces(grp, a.NG, rb, a.nrb, total, b_first, off_first, units, fn);
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   lds_char* tiles = (lds_char*)smem;
-  int32_t* off = (int32_t*)(smem + kTileBufs * kTileBytes);
-  // Tiles a load skips keep what is in LDS; start from zeros.
-  for (int i = threadIdx.x; i < kTileBufs * kTileBytes / 16; i += kSplitThreads)
-    ((__attribute__((address_space(3))) u32x4_t*)tiles)[i] = u32x4_t{0u, 0u, 0u, 0u};
-  Stage<FP8> stg;
-  stg.init();
-  LaneOffsets lo_;
-  lo_.init();
   int64_t grp;
   int32_t rb;
   group_of_block(blockIdx.x, a.nrb, &grp, &rb);
-  if (a.num_splits > 0) {
-    __syncthreads();
-    if (grp >= a.NG) return;
-    const int32_t b = (int32_t)(grp / a.num_splits);
-    const int32_t U = units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
-    Piece pc;
-    if (forced_piece(grp, rb, a.nrb, a.num_splits, U, &pc)) run_piece<FP8>(a, tiles, stg, lo_, pc);
-    return;
+  // Balanced mode: the unit offsets of all requests are built in the tile
+  // buffers' LDS (before any tile is loaded), block 0 publishes them for the
+  // combine, and this workgroup keeps only where its share starts.
+  int32_t total = 0, b_first = 0, off_first = 0;
+  if (a.num_splits == 0) {
+    int32_t* off = (int32_t*)smem;
+    build_unit_offsets<kSplitThreads>(a.seq_lens, a.B, a.max_seq_len, off);
+    if (blockIdx.x == 0)
+      for (int b = threadIdx.x; b <= a.B; b += kSplitThreads) a.unit_off_ws[b] = off[b];
+    total = __builtin_amdgcn_readfirstlane(off[a.B]);
+    const int64_t u_begin = wg_start(grp, total, a.NG);
+    if (u_begin < total) {
+      b_first = __builtin_amdgcn_readfirstlane(find_request(off, a.B, u_begin));
+      off_first = __builtin_amdgcn_readfirstlane(off[b_first]);
+    }
+    __syncthreads();   // every wave has read the offsets before the buffers are cleared
   }
-  build_unit_offsets<kSplitThreads>(a.seq_lens, a.B, a.max_seq_len, off);
-  if (blockIdx.x == 0)
-    for (int b = threadIdx.x; b <= a.B; b += kSplitThreads) a.unit_off_ws[b] = off[b];
+  // Tiles a load skips keep what is in LDS; start from zeros.
+  for (int i = threadIdx.x; i < kTileBufs * kTileBytes / 16; i += kSplitThreads)
+    ((__attribute__((address_space(3))) u32x4_t*)tiles)[i] = u32x4_t{0u, 0u, 0u, 0u};
+  lds_barrier();
   if (grp >= a.NG) return;
-  auto uo = [&](int32_t b) -> int64_t { return off[b]; };
-  auto fr = [&](int64_t u) -> int32_t { return find_request(off, a.B, u); };
-  balanced_pieces(grp, a.NG, rb, a.nrb, uo, fr, a.B,
-                  [&](const Piece& pc) { run_piece<FP8>(a, tiles, stg, lo_, pc); });
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave >= kComputeWaves) {
+    const int lw = wave - kComputeWaves;
+    Stage<FP8> stg;
+    stg.init(lw);
+    for_each_piece<FP8>(a, grp, rb, total, b_first, off_first,
+                        [&](const Piece& pc) { load_piece<FP8>(a, tiles, stg, pc, lw); });
+  } else {
+    LaneOffsets lo_;
+    lo_.init();
+    for_each_piece<FP8>(a, grp, rb, total, b_first, off_first,
+                        [&](const Piece& pc) { compute_piece<FP8>(a, tiles, lo_, pc); });
+  }
 }
 
 // ---- combine: merge the partial results of each split row block by LSE
@@ -861,9 +931,11 @@ __global__ __launch_bounds__(kThreads) void mla_plan_kernel(const int32_t* seq_l
     Piece pc;
     if (forced_piece(grp, rb, nrb, num_splits, units_of(clamp_len(seq_lens[b], max_seq_len)), &pc)) emit(pc);
   } else {
-    auto uo = [&](int32_t b) -> int64_t { return off[b]; };
-    auto fr = [&](int64_t u) -> int32_t { return find_request(off, B, u); };
-    balanced_pieces(grp, NG, rb, nrb, uo, fr, B, emit);
+    const int32_t total = off[B];
+    const int64_t u_begin = wg_start(grp, total, NG);
+    const int32_t b_first = u_begin < total ? find_request(off, B, u_begin) : 0;
+    auto units = [&](int32_t b) -> int32_t { return units_of(clamp_len(seq_lens[b], max_seq_len)); };
+    balanced_pieces(grp, NG, rb, nrb, total, b_first, off[b_first], units, emit);
   }
   if (threadIdx.x == 0) counts[wg] = n;
 }
@@ -874,7 +946,11 @@ __global__ __launch_bounds__(kThreads) void mla_plan_kernel(const int32_t* seq_l
 extern "C" {
 
 size_t mla_split_lds_bytes(int32_t B, int32_t num_splits) {
-  return (size_t)mla::kTileBufs * mla::kTileBytes + (num_splits > 0 ? 0 : ((size_t)B + 1) * 4);
+  (void)B;
+  (void)num_splits;
+  static_assert((mla::kMaxBatch + 1) * 4 <= mla::kTileBufs * mla::kTileBytes,
+                "the planning scan keeps B+1 offsets in the tile buffers");
+  return (size_t)mla::kTileBufs * mla::kTileBytes;
 }
 
 hipError_t mla_launch_split(const mla::SplitArgs* a, int fp8, hipStream_t stream) {

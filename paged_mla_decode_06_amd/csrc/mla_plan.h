@@ -38,7 +38,7 @@ constexpr int kRowDim = 576;       // latent 512 + rope 64
 constexpr int kLatentDim = 512;
 constexpr int kTile = 32;          // tokens per KV tile
 constexpr int kRowsPerBlock = 64;  // query rows per workgroup (4 waves x 16)
-constexpr int kMaxBatch = 8192;    // bounded by the LDS that holds the plan next to the KV tiles
+constexpr int kMaxBatch = 8192;    // the planning scan keeps (B+1) offsets in the tile buffers' LDS
 constexpr int kXcds = 8;           // workgroup i is dispatched to XCD i mod 8
 
 MLA_HD int32_t clamp_len(int32_t L, int32_t max_seq_len) {
@@ -84,21 +84,24 @@ struct Piece {
   int32_t b, rb, tile0, tile1, slot;
 };
 
-// Pieces of balanced-mode group g for row block rb.  unit_off(b) = sum_{b' <
-// b} U_b' for b in [0, B]; `find(u)` returns the request b with unit_off(b) <=
-// u < unit_off(b+1).  fn(Piece) is called for each piece in order.
-template <class Off, class Find, class Fn>
-MLA_HD void balanced_pieces(int64_t g, int64_t G, int32_t rb, int32_t nrb, const Off& unit_off, const Find& find,
-                            int32_t B, Fn&& fn) {
-  const int64_t total = unit_off(B);
+// Pieces of balanced-mode group g for row block rb.  total is the number of
+// units of all requests; b_first is the request holding the group's first
+// unit start(g) (off(b_first) <= start(g) < off(b_first + 1), off(b) = sum of
+// U_b' for b' < b) and off_first = off(b_first); units(b) returns U_b.  The
+// requests of the share are walked in order, so no table of offsets is
+// needed.  fn(Piece) is called for each piece in order.
+template <class Units, class Fn>
+MLA_HD void balanced_pieces(int64_t g, int64_t G, int32_t rb, int32_t nrb, int64_t total, int32_t b_first,
+                            int64_t off_first, const Units& units, Fn&& fn) {
   const int64_t u_begin = wg_start(g, total, G), u_end = wg_start(g + 1, total, G);
   if (u_begin >= u_end) return;
   const int64_t wg = g * nrb + rb;
-  int32_t b = find(u_begin);
+  int32_t b = b_first;
+  int64_t ob = off_first;
   int64_t u = u_begin;
   while (u < u_end) {
-    const int64_t ob = unit_off(b), oe = unit_off(b + 1);
-    const int32_t U = (int32_t)(oe - ob);
+    const int32_t U = units(b);
+    const int64_t oe = ob + U;
     const int64_t pe = oe < u_end ? oe : u_end;
     Piece pc;
     pc.b = b;
@@ -109,6 +112,7 @@ MLA_HD void balanced_pieces(int64_t g, int64_t G, int32_t rb, int32_t nrb, const
     pc.slot = whole ? -1 : (int32_t)(2 * wg + (u == u_begin ? 0 : 1));
     fn(pc);
     u = pe;
+    ob = oe;
     b++;
   }
 }
