@@ -352,6 +352,40 @@ struct Stage<true> {
   }
 };
 
+#ifndef MLA_PERMLANE
+#define MLA_PERMLANE 1
+#endif
+// Reductions over the four lanes l, l^16, l^32, l^48 that hold one query row.
+// The gfx950 lane swaps are plain VALU operations; each returns the two
+// swapped registers, and combining both gives the partner's value in every
+// lane.
+__device__ __forceinline__ float row_max4(float x) {
+#if MLA_PERMLANE
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+  const uint32_t v = __builtin_bit_cast(uint32_t, x);
+  const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)q[0]), __builtin_bit_cast(float, (uint32_t)q[1]));
+#else
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+#endif
+}
+__device__ __forceinline__ float row_sum4(float x) {
+#if MLA_PERMLANE
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+  const uint32_t v = __builtin_bit_cast(uint32_t, x);
+  const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return __builtin_bit_cast(float, (uint32_t)q[0]) + __builtin_bit_cast(float, (uint32_t)q[1]);
+#else
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+#endif
+}
+
 // An LDS address the optimiser cannot look into: per-read constant offsets
 // then fold into the DS instructions instead of being re-added to the tile
 // buffer arithmetic for every read.
@@ -505,23 +539,21 @@ __device__ __forceinline__ void tile_step(const bf16x8_t (&qf)[kRowBlocksPerWave
       s0 += sp[rb][0][1];
       s1 += sp[rb][1][1];
     }
-    float x[8];
-    if (!masked) {
+    // raw scores of the lane's 8 tokens; masked tokens become -inf
+    float sv[8];
 #pragma unroll
-      for (int e = 0; e < 8; e++) x[e] = (e < 4 ? s0[e & 3] : s1[e & 3]) * scale_log2;
-    } else {
+    for (int e = 0; e < 8; e++) sv[e] = e < 4 ? s0[e & 3] : s1[e & 3];
+    if (masked) {
 #pragma unroll
       for (int e = 0; e < 8; e++) {
         const int t = ts + 16 * (e >> 2) + 4 * g + (e & 3);
-        const float sv = e < 4 ? s0[e & 3] : s1[e & 3];
-        x[e] = t < limit[rb] ? sv * scale_log2 : kNegInf;
+        sv[e] = t < limit[rb] ? sv[e] : kNegInf;
       }
     }
-    float mx = kNegInf;
-#pragma unroll
-    for (int e = 0; e < 8; e++) mx = fmaxf(mx, x[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // row maximum in log2 units: the scale is positive, so it is taken on the
+    // raw scores and scaled once
+    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    mx = row_max4(mx) * scale_log2;
     const bool need = mx > st.m_run[rb] + kRescaleSlack;
     if (__any(need)) {
       const float m_new = need ? mx : st.m_run[rb];
@@ -535,8 +567,8 @@ __device__ __forceinline__ void tile_step(const bf16x8_t (&qf)[kRowBlocksPerWave
     u32x4_t pk;
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-      const float p0 = __builtin_amdgcn_exp2f(x[2 * e] - m_use);
-      const float p1 = __builtin_amdgcn_exp2f(x[2 * e + 1] - m_use);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * e], scale_log2, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * e + 1], scale_log2, -m_use));
       psum += p0 + p1;
       pk[e] = (uint32_t)f32_to_bf16_rne(p0) | ((uint32_t)f32_to_bf16_rne(p1) << 16);
     }
@@ -678,8 +710,7 @@ __device__ void compute_piece(const SplitArgs& a, lds_char* lds, const LaneOffse
   static_assert(kRowsPerBlock * kStagePitch <= kTileBufs * kTileBytes, "staged rows fit the tile buffers");
 #pragma unroll
   for (int rb = 0; rb < RB; rb++) {
-    float l_tot = st.l_run[rb] + __shfl_xor(st.l_run[rb], 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = row_sum4(st.l_run[rb]);
     const bool empty = !(l_tot > 0.f);
     const float inv = empty ? 0.f : a.out_scale / l_tot;
     const float lse_nat = empty ? kNegInf : (st.m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
@@ -849,33 +880,84 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(CombineArgs a) {
     return balanced_slot(g, g0, first_unit, total, a.NG, rb, a.nrb);
   };
   const int64_t n = g1 - g0 + 1;
-  // pass 1: maximum LSE over the pieces, 64 pieces per step
-  float M = kNegInf;
-  for (int64_t c0 = 0; c0 < n; c0 += 64) {
-    const int64_t s = c0 + lane < n ? slot_of(g0 + c0 + lane) : -1;
-    const float ls = s >= 0 ? a.part_lse[s * kRowsPerBlock + row_in_blk] : kNegInf;
-    M = fmaxf(M, ls);
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
-  // pass 2: weighted sum; lane l owns dims 8l..8l+7
+  // Lane l handles piece c0 + l of each chunk of 64: its slot, its LSE and
+  // its weight exp(lse - M).  Partial rows are then loaded eight at a time
+  // (lane l owns dims 8l..8l+7) so that their latencies overlap; a missing
+  // piece reads slot 0 with weight 0 and is dropped by a select (that slot
+  // may hold anything).  With at most 64 pieces the first eight rows are
+  // loaded together with the LSEs, before the maximum is known.
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  if (M != kNegInf) {
-    for (int64_t i = 0; i < n; i++) {
-      const int64_t s = slot_of(g0 + i);
-      if (s < 0) continue;
-      const float ls = a.part_lse[s * kRowsPerBlock + row_in_blk];
-      const float w = ls == kNegInf ? 0.f : __expf(ls - M);
-      den += w;
-      const u32x4_t v = *(const u32x4_t*)(a.part_o + (s * kRowsPerBlock + row_in_blk) * kLatentDim + 8 * lane);
+  auto load8 = [&](int32_t s32, int j, u32x4_t (&v)[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int32_t sk = __builtin_amdgcn_readlane(s32, min(j + k, 63));
+      v[k] = *(const u32x4_t*)(a.part_o + ((int64_t)sk * kRowsPerBlock + row_in_blk) * kLatentDim + 8 * lane);
+    }
+  };
+  auto accum8 = [&](float w, int j, int cnt, const u32x4_t (&v)[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const float wk = j + k < cnt ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int32_t, w),
+                                                                                          min(j + k, 63)))
+                                   : 0.f;
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        o[2 * e] += w * __builtin_bit_cast(float, v[e] << 16);
-        o[2 * e + 1] += w * __builtin_bit_cast(float, v[e] & 0xFFFF0000u);
+        const float lo = wk * __builtin_bit_cast(float, v[k][e] << 16);
+        const float hi = wk * __builtin_bit_cast(float, v[k][e] & 0xFFFF0000u);
+        o[2 * e] += wk != 0.f ? lo : 0.f;
+        o[2 * e + 1] += wk != 0.f ? hi : 0.f;
+      }
+    }
+  };
+  float M = kNegInf;
+  if (n <= 64) {
+    const int64_t s = lane < n ? slot_of(g0 + lane) : -1;
+    const int32_t s32 = s >= 0 ? (int32_t)s : 0;
+    const float ls = s >= 0 ? a.part_lse[s * kRowsPerBlock + row_in_blk] : kNegInf;
+    u32x4_t v[8];
+    load8(s32, 0, v);
+    M = ls;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
+    if (M != kNegInf) {
+      const float w = ls == kNegInf ? 0.f : __expf(ls - M);
+      den = w;
+      const int cnt = (int)n;
+      accum8(w, 0, cnt, v);
+      for (int j = 8; j < cnt; j += 8) {
+        load8(s32, j, v);
+        accum8(w, j, cnt, v);
+      }
+    }
+  } else {
+    // pass 1: maximum LSE over the pieces
+    for (int64_t c0 = 0; c0 < n; c0 += 64) {
+      const int64_t s = c0 + lane < n ? slot_of(g0 + c0 + lane) : -1;
+      const float ls = s >= 0 ? a.part_lse[s * kRowsPerBlock + row_in_blk] : kNegInf;
+      M = fmaxf(M, ls);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
+    // pass 2: weighted sum
+    if (M != kNegInf) {
+      for (int64_t c0 = 0; c0 < n; c0 += 64) {
+        const int64_t s = c0 + lane < n ? slot_of(g0 + c0 + lane) : -1;
+        const int32_t s32 = s >= 0 ? (int32_t)s : 0;
+        const float ls = s >= 0 ? a.part_lse[s * kRowsPerBlock + row_in_blk] : kNegInf;
+        const float w = ls == kNegInf ? 0.f : __expf(ls - M);
+        den += w;
+        const int cnt = (int)min((int64_t)64, n - c0);
+        for (int j = 0; j < cnt; j += 8) {
+          u32x4_t v[8];
+          load8(s32, j, v);
+          accum8(w, j, cnt, v);
+        }
       }
     }
   }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) den += __shfl_xor(den, d);
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int32_t jq = row / a.H, h = row - jq * a.H;
   const int64_t orow = (int64_t)(b * a.q_len + jq) * a.H + h;
