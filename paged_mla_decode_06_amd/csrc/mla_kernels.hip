@@ -45,7 +45,7 @@ constexpr int kThreads = 256;                      // combine / gather / plan ke
 #endif
 constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
 #ifndef MLA_KA
-#define MLA_KA 4
+#define MLA_KA 6
 #endif
 #ifndef MLA_VA
 #define MLA_VA 4
@@ -54,26 +54,33 @@ constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
 #define MLA_SC 2
 #endif
 #ifndef MLA_F8_KA
-#define MLA_F8_KA 4
+#define MLA_F8_KA 8
 #endif
 #ifndef MLA_F8_VA
 #define MLA_F8_VA 4
 #endif
 #ifndef MLA_F8_SC
-#define MLA_F8_SC 2
+#define MLA_F8_SC 4
 #endif
 constexpr int kRowsPerWave = 16 * kRowBlocksPerWave;
-// A split workgroup has kComputeWaves waves that own the query rows and do
-// the MFMA work, and kLoaderWaves waves that only move KV tiles into LDS.
-// A tile load can stall its wave at issue for hundreds of cycles while the
-// memory queue is full; with separate loader waves that stall never holds up
-// a compute wave (each SIMD runs one wave of each kind).
-constexpr int kComputeWaves = kRowsPerBlock / kRowsPerWave;
+static_assert(kRowBlocksPerWave == 1, "one 16-row MFMA block per wave");
+// A split workgroup runs three kinds of wave, kRowGroups of each (one of each
+// kind per SIMD), in a pipeline over the KV tiles of a piece:
+//   QK waves      S = Q.K^T for their 16 rows on tile j+1, online softmax,
+//                 P (bf16) and the rows' rescale factors out to LDS;
+//   PV waves      the same 16 rows: O = alpha*O + P.V on tile j;
+//   loader waves  tile j+3 into the LDS ring.
+// Splitting the two products over two waves gives each one registers for a
+// deep LDS read-ahead (Q and O no longer share a wave), and the softmax of
+// one wave runs while the other keeps the matrix unit busy.  A tile load can
+// stall its wave at issue for hundreds of cycles while the memory queue is
+// full; the loader waves take those stalls.
+constexpr int kRowGroups = kRowsPerBlock / kRowsPerWave;
+constexpr int kQKWave0 = 0, kPVWave0 = kRowGroups, kLoaderWave0 = 2 * kRowGroups;
 constexpr int kLoaderWaves = 4;
-constexpr int kSplitWaves = kComputeWaves + kLoaderWaves;
+constexpr int kSplitWaves = 2 * kRowGroups + kLoaderWaves;
 constexpr int kSplitThreads = 64 * kSplitWaves;
 constexpr int kLoaderThreads = 64 * kLoaderWaves;
-static_assert(kComputeWaves * kRowsPerWave == kRowsPerBlock, "compute waves must tile the row block");
 constexpr int kRowBytes = kRowDim * 2;             // 1152: one bf16 row in LDS
 constexpr int kTileBytes = kTile * kRowBytes;      // 36864
 constexpr int kChunks = kTile * kRowDim * 2 / 16;  // 2304 16-byte chunks per bf16 tile
@@ -93,6 +100,13 @@ static_assert(kChunks % 64 == 0, "tile must be a whole number of wave-wide loads
 static_assert(kTileLoads % kLoaderWaves == 0, "every loader wave issues the same number of tile loads");
 // KV tile buffers in LDS: kTileBufs - 1 tiles are in flight while one is consumed.
 constexpr int kTileBufs = 4;
+// LDS of a split workgroup: the tile ring, then two sets of P fragments
+// (one 1 KB block per QK wave: its lanes' bf16x8 B operands), two sets of
+// rescale factors (16 floats per QK wave) and the rows' final max / sum.
+constexpr int kPBufOff = kTileBufs * kTileBytes;
+constexpr int kABufOff = kPBufOff + 2 * kRowGroups * 1024;
+constexpr int kStatsOff = kABufOff + 2 * kRowGroups * 64;
+constexpr int kSplitLdsBytes = kStatsOff + kRowsPerBlock * 8;
 static_assert(kTile == 32, "the MFMA layout below assumes 32-token tiles");
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -320,7 +334,7 @@ struct Stage<true> {
   __device__ __forceinline__ void init(int) {}
   // Called by the loader waves; lt = thread index among them.
   __device__ __forceinline__ void load(const SplitArgs& a, PageWindow& pw, int b, int ts, int tok_end) {
-    const int lt = threadIdx.x - 64 * kComputeWaves;
+    const int lt = threadIdx.x - 64 * kLoaderWave0;
     const char* base = nullptr;
     if (ts < tok_end) {
       const int32_t page = pw.page(a, b, ts / a.P);
@@ -336,7 +350,7 @@ struct Stage<true> {
     }
   }
   __device__ __forceinline__ void store(lds_char* buf) const {
-    const int lt = threadIdx.x - 64 * kComputeWaves;
+    const int lt = threadIdx.x - 64 * kLoaderWave0;
 #pragma unroll
     for (int i = 0; i < kFp8PerThread; i++) {
       const int ci = lt + kLoaderThreads * i;
@@ -398,38 +412,6 @@ __device__ __forceinline__ lds_cchar* opaque_lds(lds_cchar* p) {
 #ifndef MLA_PIN_ORDER
 #define MLA_PIN_ORDER 1
 #endif
-#ifndef MLA_ACC_IN_AGPR
-#define MLA_ACC_IN_AGPR 0
-#endif
-// O *= alpha for one row block's accumulators.  With MLA_ACC_IN_AGPR the
-// accumulators live in AGPRs (the only way 32 rows of O and Q fit one wave):
-// each element is read, scaled and written back inside one asm statement
-// whose AGPR constraint keeps the register allocator from moving O into
-// VGPRs.  The s_nop guards cover the MFMA-result and AGPR-write hazards the
-// compiler cannot see inside the asm; this path runs only when a row's
-// running maximum grows, so they cost nothing in the steady state.
-__device__ __forceinline__ void rescale_acc(f32x4v_t (&acc)[kVBlocks], float alpha) {
-#if MLA_ACC_IN_AGPR
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#pragma unroll
-  for (int mb = 0; mb < kVBlocks; mb++) {
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      float x = acc[mb][e];
-      float t;
-      asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                   : "+a"(x), "=&v"(t)
-                   : "v"(alpha));
-      acc[mb][e] = x;
-    }
-  }
-  asm volatile("s_nop 7" ::: "memory");
-#else
-#pragma unroll
-  for (int mb = 0; mb < kVBlocks; mb++) acc[mb] *= alpha;
-#endif
-}
-
 __device__ __forceinline__ s16x4_t lds_read_tr16(lds_cchar* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
 }
@@ -437,14 +419,6 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(lds_cchar* p) {
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
-
-// Per-wave running state: kRowBlocksPerWave blocks of 16 rows, lane l owns
-// row l%16 of each block.
-struct RowState {
-  f32x4v_t acc[kRowBlocksPerWave][kVBlocks];   // O^T: row l%16, dims 16*mb + 4*(l/16) + r
-  float m_run[kRowBlocksPerWave];              // running max of the row's scaled scores (log2 units)
-  float l_run[kRowBlocksPerWave];              // this lane's share of the softmax denominator
-};
 
 constexpr int kQKSteps = 2 * kQSteps;   // (token block, k-step) pairs of S^T = K . Q^T
 
@@ -473,109 +447,112 @@ struct LaneOffsets {
   }
 };
 
-// One KV tile for one wave: S^T, online softmax, O^T update for each of the
-// wave's RB row blocks.  Every K fragment and V^T fragment read from LDS
-// feeds the MFMAs of all RB blocks.  The LDS reads run kKAhead K fragments /
-// kVAhead V^T fragments (two transposing reads each) ahead of their MFMA so
-// that the matrix unit and the LDS pipe stay busy together; the depths are
-// what fits the register file next to the Q fragments and O accumulators.
-template <int kKAhead, int kVAhead, int kSChains>
-__device__ __forceinline__ void tile_step(const bf16x8_t (&qf)[kRowBlocksPerWave][kQSteps], RowState& st,
-                                          lds_cchar* cur, const LaneOffsets& lo_, int ts,
-                                          const int (&limit)[kRowBlocksPerWave], int lim_min, float scale_log2) {
-  constexpr int RB = kRowBlocksPerWave;
+// QK wave, one tile: S^T[32 tokens x 16 rows] = K_tile . Q^T (36 MFMA), the
+// online softmax of the lane's 8 tokens of its row, then P^T (the B operand
+// of the P.V product, 16 bytes per lane) and the row's rescale factor alpha
+// to LDS for the PV wave of the same rows.  The K reads run kKAhead steps
+// ahead of their MFMA.
+template <int kKAhead, int kSChains>
+__device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[kQSteps], float& m_run, float& l_run, lds_cchar* cur,
+                                        const LaneOffsets& lo_, int ts, int limit, int lim_min, float scale_log2,
+                                        lds_char* pout, lds_char* aout) {
   static_assert(kSChains == 2 || kSChains == 4, "one or two accumulation chains per token block");
   constexpr int kCh = kSChains / 2;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   lds_cchar* kp[2] = {opaque_lds(cur + lo_.kbase[0]), opaque_lds(cur + lo_.kbase[1])};
-  lds_cchar* vp[4] = {opaque_lds(cur + lo_.vbase[0]), opaque_lds(cur + lo_.vbase[1]),
-                      opaque_lds(cur + lo_.vbase[2]), opaque_lds(cur + lo_.vbase[3])};
   // every token of the tile is visible to every row of the wave: no mask
   const bool masked = ts + kTile > lim_min;
   auto kread = [&](int s) -> bf16x8_t {
     const int k = s >> 1, tb = s & 1;
     return *(__attribute__((address_space(3))) const bf16x8_t*)(kp[k & 1] + 18432 * tb + 128 * (k >> 1));
   };
-  auto vread = [&](int mb, int second) -> u32x2_t {
-    return __builtin_bit_cast(u32x2_t, lds_read_tr16(vp[mb & 3] + 18432 * second + 128 * (mb >> 2)));
-  };
-  // ---- S^T = K . Q^T: two 16-token blocks, kCh accumulation chains each
   bf16x8_t kb[kKAhead];
 #pragma unroll
   for (int s = 0; s < kKAhead; s++) kb[s] = kread(s);
-  f32x4v_t sp[RB][2][kCh];
+  f32x4v_t sp[2][kCh];
 #pragma unroll
-  for (int rb = 0; rb < RB; rb++)
+  for (int tb = 0; tb < 2; tb++)
 #pragma unroll
-    for (int tb = 0; tb < 2; tb++)
-#pragma unroll
-      for (int c = 0; c < kCh; c++) sp[rb][tb][c] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < kCh; c++) sp[tb][c] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kQKSteps; s++) {
     const bf16x8_t kf = kb[s % kKAhead];
     if (s + kKAhead < kQKSteps) kb[s % kKAhead] = kread(s + kKAhead);
     const int k = s >> 1, tb = s & 1;
-#pragma unroll
-    for (int rb = 0; rb < RB; rb++)
-      sp[rb][tb][k % kCh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][k], sp[rb][tb][k % kCh], 0, 0, 0);
+    sp[tb][k % kCh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[k], sp[tb][k % kCh], 0, 0, 0);
     // keep each step's read kKAhead steps ahead of its MFMA: left alone, the
     // scheduler sinks the reads next to their use and exposes the LDS latency
     if (MLA_PIN_ORDER) __builtin_amdgcn_sched_barrier(0);
   }
-  // V^T reads do not depend on P: start them before the softmax
+  f32x4v_t s0 = sp[0][0], s1 = sp[1][0];
+  if constexpr (kCh == 2) {
+    s0 += sp[0][1];
+    s1 += sp[1][1];
+  }
+  // raw scores of the lane's 8 tokens; masked tokens become -inf
+  float sv[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) sv[e] = e < 4 ? s0[e & 3] : s1[e & 3];
+  if (masked) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const int t = ts + 16 * (e >> 2) + 4 * g + (e & 3);
+      sv[e] = t < limit ? sv[e] : kNegInf;
+    }
+  }
+  // row maximum in log2 units: the scale is positive, so it is taken on the
+  // raw scores and scaled once.  The running maximum is raised only when a
+  // tile's maximum exceeds it by more than kRescaleSlack.
+  float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+  mx = row_max4(mx) * scale_log2;
+  float alpha = 1.f;
+  const bool need = mx > m_run + kRescaleSlack;
+  if (__any(need)) {
+    const float m_new = need ? mx : m_run;
+    alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // m_run = -inf gives 0
+    l_run *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = m_run == kNegInf ? 0.f : m_run;
+  float psum = 0.f;
+  u32x4_t pk;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * e], scale_log2, -m_use));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * e + 1], scale_log2, -m_use));
+    psum += p0 + p1;
+    pk[e] = (uint32_t)f32_to_bf16_rne(p0) | ((uint32_t)f32_to_bf16_rne(p1) << 16);
+  }
+  l_run += psum;
+  *(__attribute__((address_space(3))) u32x4_t*)(pout + 16 * lane) = pk;
+  if (lane < 16) *(__attribute__((address_space(3))) float*)(aout + 4 * lane) = alpha;
+}
+
+// PV wave, one tile: O^T[512 x 16 rows] = alpha * O^T + V^T[512 x 32] . P^T
+// (32 MFMA), V^T from the same LDS tile through the transposing read, kVAhead
+// blocks ahead of their MFMA.
+template <int kVAhead>
+__device__ __forceinline__ void pv_tile(f32x4v_t (&acc)[kVBlocks], lds_cchar* cur, const LaneOffsets& lo_,
+                                        lds_cchar* pin, lds_cchar* ain) {
+  const int lane = threadIdx.x & 63;
+  lds_cchar* vp[4] = {opaque_lds(cur + lo_.vbase[0]), opaque_lds(cur + lo_.vbase[1]),
+                      opaque_lds(cur + lo_.vbase[2]), opaque_lds(cur + lo_.vbase[3])};
+  auto vread = [&](int mb, int second) -> u32x2_t {
+    return __builtin_bit_cast(u32x2_t, lds_read_tr16(vp[mb & 3] + 18432 * second + 128 * (mb >> 2)));
+  };
   u32x2_t vb[kVAhead][2];
 #pragma unroll
   for (int m = 0; m < kVAhead; m++) {
     vb[m][0] = vread(m, 0);
     vb[m][1] = vread(m, 1);
   }
-  // ---- online softmax over the lane's 8 tokens of its row, per row block
-  bf16x8_t pf[RB];
+  const bf16x8_t pf = *(__attribute__((address_space(3))) const bf16x8_t*)(pin + 16 * lane);
+  const float alpha = *(__attribute__((address_space(3))) const float*)(ain + 4 * (lane & 15));
+  if (__any(alpha != 1.f)) {
 #pragma unroll
-  for (int rb = 0; rb < RB; rb++) {
-    f32x4v_t s0 = sp[rb][0][0], s1 = sp[rb][1][0];
-    if constexpr (kCh == 2) {
-      s0 += sp[rb][0][1];
-      s1 += sp[rb][1][1];
-    }
-    // raw scores of the lane's 8 tokens; masked tokens become -inf
-    float sv[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++) sv[e] = e < 4 ? s0[e & 3] : s1[e & 3];
-    if (masked) {
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const int t = ts + 16 * (e >> 2) + 4 * g + (e & 3);
-        sv[e] = t < limit[rb] ? sv[e] : kNegInf;
-      }
-    }
-    // row maximum in log2 units: the scale is positive, so it is taken on the
-    // raw scores and scaled once
-    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mx = row_max4(mx) * scale_log2;
-    const bool need = mx > st.m_run[rb] + kRescaleSlack;
-    if (__any(need)) {
-      const float m_new = need ? mx : st.m_run[rb];
-      const float alpha = need ? __builtin_amdgcn_exp2f(st.m_run[rb] - m_new) : 1.f;   // m_run = -inf gives 0
-      st.l_run[rb] *= alpha;
-      rescale_acc(st.acc[rb], alpha);
-      st.m_run[rb] = m_new;
-    }
-    const float m_use = st.m_run[rb] == kNegInf ? 0.f : st.m_run[rb];
-    float psum = 0.f;
-    u32x4_t pk;
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * e], scale_log2, -m_use));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * e + 1], scale_log2, -m_use));
-      psum += p0 + p1;
-      pk[e] = (uint32_t)f32_to_bf16_rne(p0) | ((uint32_t)f32_to_bf16_rne(p1) << 16);
-    }
-    st.l_run[rb] += psum;
-    pf[rb] = __builtin_bit_cast(bf16x8_t, pk);
+    for (int mb = 0; mb < kVBlocks; mb++) acc[mb] *= alpha;
   }
-  // ---- O^T += V^T . P^T
 #pragma unroll
   for (int mb = 0; mb < kVBlocks; mb++) {
     const u32x2_t lo = vb[mb % kVAhead][0], hi = vb[mb % kVAhead][1];
@@ -584,16 +561,21 @@ __device__ __forceinline__ void tile_step(const bf16x8_t (&qf)[kRowBlocksPerWave
       vb[mb % kVAhead][1] = vread(mb + kVAhead, 1);
     }
     const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-    for (int rb = 0; rb < RB; rb++)
-      st.acc[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb], st.acc[rb][mb], 0, 0, 0);
+    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[mb], 0, 0, 0);
     if (MLA_PIN_ORDER) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// The loader waves' side of one piece: the piece's KV tiles into the LDS
-// ring, in step with the compute waves' barriers (one per tile, then the two
-// around the epilogue).
+// The pipeline of one piece runs in intervals j = -1 .. nt-1, each opened by
+// a workgroup barrier; in interval j the QK waves take tile j+1, the PV waves
+// tile j, and the loaders issue tile j+3 into the buffer of tile j-1 (free:
+// the PV waves finished it in interval j-1, the QK waves in j-2).  Two more
+// barriers close the piece: after the first the QK waves' final row max and
+// sum are in LDS and every tile is done; after the second the PV waves have
+// read the output rows they staged in the tile buffers.
+__device__ __forceinline__ int tile_buf(int t) { return t & (kTileBufs - 1); }
+static_assert((kTileBufs & (kTileBufs - 1)) == 0, "tile_buf masks the tile index");
+
 template <bool FP8>
 __device__ void load_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, const Piece& pc, int lw) {
   const int b = pc.b;
@@ -602,148 +584,146 @@ __device__ void load_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, c
   const int nt = pc.tile1 - pc.tile0;
   PageWindow pw;
   pw.init(a, b, (pc.tile0 * kTile) / a.P, (tok_end + a.P - 1) / a.P);
-  if constexpr (FP8) {
-    // two LDS buffers: tile it+1 is converted in while tile it is consumed,
-    // tile it+2 waits in registers
-    stg.load(a, pw, b, pc.tile0 * kTile, tok_end);
-    stg.store(lds);
-    if (nt > 1) stg.load(a, pw, b, (pc.tile0 + 1) * kTile, tok_end);
-    for (int it = 0; it < nt; it++) {
-      lds_barrier();
-      if (it + 1 < nt) stg.store(lds + ((it + 1) & 1) * kTileBytes);
-      if (it + 2 < nt) stg.load(a, pw, b, (pc.tile0 + it + 2) * kTile, tok_end);
+  auto put = [&](int t) {   // tile t of the piece into its ring buffer
+    if constexpr (FP8) {
+      stg.load(a, pw, b, (pc.tile0 + t) * kTile, tok_end);
+      stg.store(lds + tile_buf(t) * kTileBytes);   // waits for its own loads
+    } else {
+      stg.issue(a, lds + tile_buf(t) * kTileBytes, pw, b, (pc.tile0 + t) * kTile, tok_end, lw);
     }
-  } else {
-    // tiles it+1 .. it+kTileBufs-1 are in flight while tile it is consumed
-#pragma unroll
-    for (int pf = 0; pf < kTileBufs - 1; pf++)
-      if (pf < nt) stg.issue(a, lds + pf * kTileBytes, pw, b, (pc.tile0 + pf) * kTile, tok_end, lw);
-    int nx_buf = kTileBufs - 1;   // buffer of tile it + kTileBufs - 1
-    for (int it = 0; it < nt; it++) {
-      stg.wait(min(nt - 1 - it, kTileBufs - 2));
-      lds_barrier();   // tile it is in LDS for every wave; the buffer of tile it-1 is free
-      const int nx = it + kTileBufs - 1;
-      if (nx < nt) stg.issue(a, lds + nx_buf * kTileBytes, pw, b, (pc.tile0 + nx) * kTile, tok_end, lw);
-      nx_buf = nx_buf == kTileBufs - 1 ? 0 : nx_buf + 1;
-    }
+  };
+  for (int t = 0; t < 2 && t < nt; t++) put(t);
+  for (int j = -1; j < nt; j++) {
+    // tile j+1 is in LDS before barrier j; tile j+2 may still be in flight
+    if constexpr (!FP8) stg.wait(j + 2 < nt ? 1 : 0);
+    lds_barrier();
+    if (j + 3 < nt) put(j + 3);
   }
-  lds_barrier();   // the compute waves are done with the tiles
-  lds_barrier();   // and with the staged output rows
+  lds_barrier();
+  lds_barrier();
 }
 
-// The compute waves' side of one piece: rows [kRowsPerBlock*rb,
-// kRowsPerBlock*(rb+1)) of request b over tiles [tile0, tile1); writes the
-// piece's output rows (or partial rows) and LSEs.
+// The QK waves' side of one piece.
 template <bool FP8>
-__device__ void compute_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& lo_, const Piece& pc) {
-  constexpr int RB = kRowBlocksPerWave;
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, i16 = lane & 15;
+__device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& lo_, const Piece& pc, int w) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
   const int b = pc.b;
   const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
   const int tok_end = min(pc.tile1 * kTile, L);
-  int row_in_blk[RB], jrow[RB], hrow[RB], limit[RB];
-  bool row_ok[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; rb++) {
-    row_in_blk[rb] = wave * kRowsPerWave + 16 * rb + i16;
-    const int row = pc.rb * kRowsPerBlock + row_in_blk[rb];
-    row_ok[rb] = row < a.R;
-    jrow[rb] = row_ok[rb] ? row / a.H : 0;
-    hrow[rb] = row_ok[rb] ? row - jrow[rb] * a.H : 0;
-    limit[rb] = min(tok_end, L - a.q_len + 1 + jrow[rb]);   // tokens t < limit are visible to this row
-  }
+  const int nt = pc.tile1 - pc.tile0;
+  const int row = pc.rb * kRowsPerBlock + 16 * w + i16;
+  const bool row_ok = row < a.R;
+  const int jrow = row_ok ? row / a.H : 0, hrow = row_ok ? row - jrow * a.H : 0;
+  const int limit = min(tok_end, L - a.q_len + 1 + jrow);   // tokens t < limit are visible to this row
   // smallest limit over the wave's rows: tiles below it need no mask
-  int lim_min = limit[0];
-#pragma unroll
-  for (int rb = 1; rb < RB; rb++) lim_min = min(lim_min, limit[rb]);
+  int lim_min = limit;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, d));
   lim_min = __builtin_amdgcn_readfirstlane(lim_min);
-
-  RowState st;
-#pragma unroll
-  for (int rb = 0; rb < RB; rb++) {
-#pragma unroll
-    for (int mb = 0; mb < kVBlocks; mb++) st.acc[rb][mb] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
-    st.m_run[rb] = kNegInf;
-    st.l_run[rb] = 0.f;
-  }
-  const int nt = pc.tile1 - pc.tile0;
-
-  // Q^T B-operand fragments: lane holds row i16 of each block, dims 32k + 8g .. +8;
-  // rows past the request's last query row load its first row and are zeroed.
+  // Q^T B-operand fragments: lane holds row i16, dims 32k + 8g .. +8; rows
+  // past the request's last query row load its first row and are zeroed.
   static_assert(kQSteps == 18, "load_q_fragments loads 18 fragments");
-  bf16x8_t qf[RB][kQSteps];
-#pragma unroll
-  for (int rb = 0; rb < RB; rb++) {
-    const int64_t qrow_id = row_ok[rb] ? (int64_t)(b * a.q_len + jrow[rb]) * a.H + hrow[rb] : (int64_t)b * a.q_len * a.H;
+  bf16x8_t qf[kQSteps];
+  {
+    const int64_t qrow_id = row_ok ? (int64_t)(b * a.q_len + jrow) * a.H + hrow : (int64_t)b * a.q_len * a.H;
     u32x4_t qv[kQSteps];
     load_q_fragments(qv, a.q + qrow_id * kRowDim + 8 * g);
 #pragma unroll
-    for (int k = 0; k < kQSteps; k++)
-      qf[rb][k] = __builtin_bit_cast(bf16x8_t, row_ok[rb] ? qv[k] : u32x4_t{0u, 0u, 0u, 0u});
+    for (int k = 0; k < kQSteps; k++) qf[k] = __builtin_bit_cast(bf16x8_t, row_ok ? qv[k] : u32x4_t{0u, 0u, 0u, 0u});
   }
-  if constexpr (FP8) {
-    for (int it = 0; it < nt; it++) {
-      lds_barrier();
-      tile_step<MLA_F8_KA, MLA_F8_VA, MLA_F8_SC>(qf, st, lds + (it & 1) * kTileBytes, lo_, (pc.tile0 + it) * kTile,
-                                                 limit, lim_min, a.scale_log2);
-    }
-  } else {
-    int cur_buf = 0;   // buffer of tile it
-    for (int it = 0; it < nt; it++) {
-      lds_barrier();   // tile it is in LDS for every wave; the buffer of tile it-1 is free
-      tile_step<MLA_KA, MLA_VA, MLA_SC>(qf, st, lds + cur_buf * kTileBytes, lo_, (pc.tile0 + it) * kTile, limit,
-                                        lim_min, a.scale_log2);
-      cur_buf = cur_buf == kTileBufs - 1 ? 0 : cur_buf + 1;
+  float m_run = kNegInf, l_run = 0.f;
+  for (int j = -1; j < nt; j++) {
+    lds_barrier();
+    const int t = j + 1;
+    if (t < nt) {
+      lds_char* pout = lds + kPBufOff + ((t & 1) * kRowGroups + w) * 1024;
+      lds_char* aout = lds + kABufOff + ((t & 1) * kRowGroups + w) * 64;
+      if constexpr (FP8)
+        qk_tile<MLA_F8_KA, MLA_F8_SC>(qf, m_run, l_run, lds + tile_buf(t) * kTileBytes, lo_, (pc.tile0 + t) * kTile,
+                                      limit, lim_min, a.scale_log2, pout, aout);
+      else
+        qk_tile<MLA_KA, MLA_SC>(qf, m_run, l_run, lds + tile_buf(t) * kTileBytes, lo_, (pc.tile0 + t) * kTile, limit,
+                                lim_min, a.scale_log2, pout, aout);
     }
   }
-  // the epilogue stages rows in the tile buffers
+  // the rows' final max (log2 units) and denominator for the PV waves
+  const float l_tot = row_sum4(l_run);
+  if (lane < 16) {
+    float* stats = (float*)(lds + kStatsOff);
+    stats[2 * (16 * w + i16)] = m_run;
+    stats[2 * (16 * w + i16) + 1] = l_tot;
+  }
   lds_barrier();
+  lds_barrier();
+}
 
-  // ---- epilogue.  Each row's denominator is spread over the 4 lane groups.
-  // The bf16 rows are staged in LDS (the tile buffers, free after the
-  // barrier above) so that every output row leaves as one contiguous 1 KB
-  // store of a wave instead of 16 rows x 32 bytes per store.
+// The PV waves' side of one piece: accumulates the rows' output and writes
+// it (or the partial result) with the LSE.
+template <bool FP8>
+__device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& lo_, const Piece& pc, int w) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
+  const int b = pc.b;
+  const int nt = pc.tile1 - pc.tile0;
+  f32x4v_t acc[kVBlocks];
+#pragma unroll
+  for (int mb = 0; mb < kVBlocks; mb++) acc[mb] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = -1; j < nt; j++) {
+    lds_barrier();
+    if (j >= 0) {
+      lds_cchar* pin = lds + kPBufOff + ((j & 1) * kRowGroups + w) * 1024;
+      lds_cchar* ain = lds + kABufOff + ((j & 1) * kRowGroups + w) * 64;
+      if constexpr (FP8)
+        pv_tile<MLA_F8_VA>(acc, lds + tile_buf(j) * kTileBytes, lo_, pin, ain);
+      else
+        pv_tile<MLA_VA>(acc, lds + tile_buf(j) * kTileBytes, lo_, pin, ain);
+    }
+  }
+  lds_barrier();   // every tile is done; the QK waves' row statistics are in LDS
+
+  // ---- epilogue.  The bf16 rows are staged in LDS (the tile buffers) so
+  // that every output row leaves as one contiguous 1 KB store of a wave
+  // instead of 16 rows x 32 bytes per store.
   constexpr int kStagePitch = kLatentDim * 2 + 16;   // rows 16 bytes apart in the banks
   static_assert(kRowsPerBlock * kStagePitch <= kTileBufs * kTileBytes, "staged rows fit the tile buffers");
+  const int rib = 16 * w + i16;   // this lane's row in the block
+  const int row = pc.rb * kRowsPerBlock + rib;
+  const float* stats = (const float*)(lds + kStatsOff);
+  const float m_run = stats[2 * rib], l_tot = stats[2 * rib + 1];
+  const bool empty = !(l_tot > 0.f);
+  const float inv = empty ? 0.f : a.out_scale / l_tot;
+  const float lse_nat = empty ? kNegInf : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  lds_char* srow = lds + rib * kStagePitch + 8 * g;
 #pragma unroll
-  for (int rb = 0; rb < RB; rb++) {
-    const float l_tot = row_sum4(st.l_run[rb]);
-    const bool empty = !(l_tot > 0.f);
-    const float inv = empty ? 0.f : a.out_scale / l_tot;
-    const float lse_nat = empty ? kNegInf : (st.m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
-    lds_char* srow = lds + row_in_blk[rb] * kStagePitch + 8 * g;
-#pragma unroll
-    for (int mb = 0; mb < kVBlocks; mb++) {
-      const f32x4v_t v = st.acc[rb][mb] * inv;
-      u32x2_t w;
-      w[0] = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-      w[1] = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-      *(__attribute__((address_space(3))) u32x2_t*)(srow + 32 * mb) = w;
-    }
-    if (row_ok[rb] && g == 0) {
-      if (pc.slot < 0) {
-        if (a.lse != nullptr) a.lse[(int64_t)(b * a.q_len + jrow[rb]) * a.H + hrow[rb]] = lse_nat;
-      } else {
-        a.part_lse[(int64_t)pc.slot * kRowsPerBlock + row_in_blk[rb]] = lse_nat;
+  for (int mb = 0; mb < kVBlocks; mb++) {
+    const f32x4v_t v = acc[mb] * inv;
+    u32x2_t wv;
+    wv[0] = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+    wv[1] = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+    *(__attribute__((address_space(3))) u32x2_t*)(srow + 32 * mb) = wv;
+  }
+  if (row < a.R && g == 0) {
+    if (pc.slot < 0) {
+      if (a.lse != nullptr) {
+        const int jq = row / a.H;
+        a.lse[(int64_t)(b * a.q_len + jq) * a.H + (row - jq * a.H)] = lse_nat;
       }
+    } else {
+      a.part_lse[(int64_t)pc.slot * kRowsPerBlock + rib] = lse_nat;
     }
   }
   // A wave copies out the rows it staged (its own LDS writes are ordered
   // before its reads): lane l carries bytes 16l .. 16l+15 of the row.
-  for (int rr = 0; rr < kRowsPerWave; rr++) {
-    const int rib = wave * kRowsPerWave + rr;
-    const int row = pc.rb * kRowsPerBlock + rib;
-    if (row >= a.R) break;
-    const u32x4_t v = *(__attribute__((address_space(3))) const u32x4_t*)(lds + rib * kStagePitch + 16 * lane);
+  for (int rr = 0; rr < 16; rr++) {
+    const int r_in = 16 * w + rr;
+    const int r = pc.rb * kRowsPerBlock + r_in;
+    if (r >= a.R) break;
+    const u32x4_t v = *(__attribute__((address_space(3))) const u32x4_t*)(lds + r_in * kStagePitch + 16 * lane);
     uint16_t* dst;
     if (pc.slot < 0) {
-      const int j = row / a.H;
-      dst = a.out + ((int64_t)(b * a.q_len + j) * a.H + (row - j * a.H)) * kLatentDim;
+      const int jq = r / a.H;
+      dst = a.out + ((int64_t)(b * a.q_len + jq) * a.H + (r - jq * a.H)) * kLatentDim;
     } else {
-      dst = a.part_o + ((int64_t)pc.slot * kRowsPerBlock + rib) * kLatentDim;
+      dst = a.part_o + ((int64_t)pc.slot * kRowsPerBlock + r_in) * kLatentDim;
     }
     *(u32x4_t*)(dst + 8 * lane) = v;
   }
@@ -832,17 +812,22 @@ __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a
   lds_barrier();
   if (grp >= a.NG) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave >= kComputeWaves) {
-    const int lw = wave - kComputeWaves;
+  if (wave >= kLoaderWave0) {
+    const int lw = wave - kLoaderWave0;
     Stage<FP8> stg;
     stg.init(lw);
     for_each_piece<FP8>(a, grp, rb, total, b_first, off_first,
                         [&](const Piece& pc) { load_piece<FP8>(a, tiles, stg, pc, lw); });
+  } else if (wave >= kPVWave0) {
+    LaneOffsets lo_;
+    lo_.init();
+    for_each_piece<FP8>(a, grp, rb, total, b_first, off_first,
+                        [&](const Piece& pc) { pv_piece<FP8>(a, tiles, lo_, pc, wave - kPVWave0); });
   } else {
     LaneOffsets lo_;
     lo_.init();
     for_each_piece<FP8>(a, grp, rb, total, b_first, off_first,
-                        [&](const Piece& pc) { compute_piece<FP8>(a, tiles, lo_, pc); });
+                        [&](const Piece& pc) { qk_piece<FP8>(a, tiles, lo_, pc, wave - kQKWave0); });
   }
 }
 
@@ -1032,16 +1017,18 @@ size_t mla_split_lds_bytes(int32_t B, int32_t num_splits) {
   (void)num_splits;
   static_assert((mla::kMaxBatch + 1) * 4 <= mla::kTileBufs * mla::kTileBytes,
                 "the planning scan keeps B+1 offsets in the tile buffers");
-  return (size_t)mla::kTileBufs * mla::kTileBytes;
+  return (size_t)mla::kSplitLdsBytes;
 }
 
 hipError_t mla_launch_split(const mla::SplitArgs* a, int fp8, hipStream_t stream) {
   const size_t lds = mla_split_lds_bytes(a->B, a->num_splits);
   static bool attr_set[2] = {false, false};
   if (!attr_set[fp8 ? 1 : 0]) {
-    // dynamic LDS above 64 KB: raise the per-kernel limit once (160 KB per workgroup on gfx950)
+    // dynamic LDS above 64 KB: raise the per-kernel limit once to what the
+    // kernel uses (static and dynamic LDS together stay within the 160 KB a
+    // gfx950 workgroup may have)
     const void* fn = fp8 ? (const void*)mla::mla_split_kernel<true> : (const void*)mla::mla_split_kernel<false>;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 2048);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)mla::kSplitLdsBytes);
     if (e != hipSuccess) return e;
     attr_set[fp8 ? 1 : 0] = true;
   }
