@@ -48,7 +48,7 @@ constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
 #define MLA_KA 6
 #endif
 #ifndef MLA_VA
-#define MLA_VA 4
+#define MLA_VA 2
 #endif
 #ifndef MLA_SC
 #define MLA_SC 2
@@ -60,7 +60,7 @@ constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
 #define MLA_F8_VA 4
 #endif
 #ifndef MLA_F8_SC
-#define MLA_F8_SC 4
+#define MLA_F8_SC 2
 #endif
 constexpr int kRowsPerWave = 16 * kRowBlocksPerWave;
 static_assert(kRowBlocksPerWave == 1, "one 16-row MFMA block per wave");
@@ -100,13 +100,13 @@ static_assert(kChunks % 64 == 0, "tile must be a whole number of wave-wide loads
 static_assert(kTileLoads % kLoaderWaves == 0, "every loader wave issues the same number of tile loads");
 // KV tile buffers in LDS: kTileBufs - 1 tiles are in flight while one is consumed.
 constexpr int kTileBufs = 4;
-// LDS of a split workgroup: the tile ring, then two sets of P fragments
-// (one 1 KB block per QK wave: its lanes' bf16x8 B operands), two sets of
-// rescale factors (16 floats per QK wave) and the rows' final max / sum.
-constexpr int kPBufOff = kTileBufs * kTileBytes;
-constexpr int kABufOff = kPBufOff + 2 * kRowGroups * 1024;
-constexpr int kStatsOff = kABufOff + 2 * kRowGroups * 64;
-constexpr int kSplitLdsBytes = kStatsOff + kRowsPerBlock * 8;
+// LDS of a split workgroup: the tile ring, then two sets of score tiles
+// (one 2 KB block per QK wave: its lanes' 8 fp32 scores) -- 160 KB in all,
+// the whole LDS of a gfx950 workgroup, so the kernel has no static LDS.
+constexpr int kSBufOff = kTileBufs * kTileBytes;
+constexpr int kSplitLdsBytes = kSBufOff + 2 * kRowGroups * 2048;
+static_assert(kSplitLdsBytes <= 160 * 1024, "split workgroup LDS");
+static_assert((kMaxBatch + 1 + 1024) * 4 <= kTileBufs * kTileBytes, "planning scan scratch fits the tile buffers");
 static_assert(kTile == 32, "the MFMA layout below assumes 32-token tiles");
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -448,21 +448,15 @@ struct LaneOffsets {
 };
 
 // QK wave, one tile: S^T[32 tokens x 16 rows] = K_tile . Q^T (36 MFMA), the
-// online softmax of the lane's 8 tokens of its row, then P^T (the B operand
-// of the P.V product, 16 bytes per lane) and the row's rescale factor alpha
-// to LDS for the PV wave of the same rows.  The K reads run kKAhead steps
-// ahead of their MFMA.
+// K reads kKAhead steps ahead of their MFMA; the lane's 8 fp32 scores (token
+// 4g + r and 16 + 4g + r of row l%16) go to LDS for the PV wave of the rows.
 template <int kKAhead, int kSChains>
-__device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[kQSteps], float& m_run, float& l_run, lds_cchar* cur,
-                                        const LaneOffsets& lo_, int ts, int limit, int lim_min, float scale_log2,
-                                        lds_char* pout, lds_char* aout) {
+__device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[kQSteps], lds_cchar* cur, const LaneOffsets& lo_,
+                                        lds_char* sout) {
   static_assert(kSChains == 2 || kSChains == 4, "one or two accumulation chains per token block");
   constexpr int kCh = kSChains / 2;
   const int lane = threadIdx.x & 63;
-  const int g = lane >> 4;
   lds_cchar* kp[2] = {opaque_lds(cur + lo_.kbase[0]), opaque_lds(cur + lo_.kbase[1])};
-  // every token of the tile is visible to every row of the wave: no mask
-  const bool masked = ts + kTile > lim_min;
   auto kread = [&](int s) -> bf16x8_t {
     const int k = s >> 1, tb = s & 1;
     return *(__attribute__((address_space(3))) const bf16x8_t*)(kp[k & 1] + 18432 * tb + 128 * (k >> 1));
@@ -490,6 +484,36 @@ __device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[kQSteps], float& m_
     s0 += sp[0][1];
     s1 += sp[1][1];
   }
+  *(__attribute__((address_space(3))) f32x4v_t*)(sout + 32 * lane) = s0;
+  *(__attribute__((address_space(3))) f32x4v_t*)(sout + 32 * lane + 16) = s1;
+}
+
+// PV wave, one tile: the online softmax of the lane's 8 scores of its row
+// (read from the QK wave's block), then O^T[512 x 16 rows] = alpha * O^T +
+// V^T[512 x 32] . P^T (32 MFMA), V^T from the same LDS tile through the
+// transposing read, kVAhead blocks ahead of their MFMA.  Running the softmax
+// here lets it overlap the QK wave's MFMAs of the next tile.
+template <int kVAhead>
+__device__ __forceinline__ void pv_tile(f32x4v_t (&acc)[kVBlocks], float& m_run, float& l_run, lds_cchar* cur,
+                                        const LaneOffsets& lo_, lds_cchar* sin, int ts, int limit, int lim_min,
+                                        float scale_log2) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  lds_cchar* vp[4] = {opaque_lds(cur + lo_.vbase[0]), opaque_lds(cur + lo_.vbase[1]),
+                      opaque_lds(cur + lo_.vbase[2]), opaque_lds(cur + lo_.vbase[3])};
+  auto vread = [&](int mb, int second) -> u32x2_t {
+    return __builtin_bit_cast(u32x2_t, lds_read_tr16(vp[mb & 3] + 18432 * second + 128 * (mb >> 2)));
+  };
+  const f32x4v_t s0 = *(__attribute__((address_space(3))) const f32x4v_t*)(sin + 32 * lane);
+  const f32x4v_t s1 = *(__attribute__((address_space(3))) const f32x4v_t*)(sin + 32 * lane + 16);
+  u32x2_t vb[kVAhead][2];
+#pragma unroll
+  for (int m = 0; m < kVAhead; m++) {
+    vb[m][0] = vread(m, 0);
+    vb[m][1] = vread(m, 1);
+  }
+  // every token of the tile is visible to every row of the wave: no mask
+  const bool masked = ts + kTile > lim_min;
   // raw scores of the lane's 8 tokens; masked tokens become -inf
   float sv[8];
 #pragma unroll
@@ -506,12 +530,13 @@ __device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[kQSteps], float& m_
   // tile's maximum exceeds it by more than kRescaleSlack.
   float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
   mx = row_max4(mx) * scale_log2;
-  float alpha = 1.f;
   const bool need = mx > m_run + kRescaleSlack;
   if (__any(need)) {
     const float m_new = need ? mx : m_run;
-    alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // m_run = -inf gives 0
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // m_run = -inf gives 0
     l_run *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < kVBlocks; mb++) acc[mb] *= alpha;
     m_run = m_new;
   }
   const float m_use = m_run == kNegInf ? 0.f : m_run;
@@ -525,34 +550,7 @@ __device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[kQSteps], float& m_
     pk[e] = (uint32_t)f32_to_bf16_rne(p0) | ((uint32_t)f32_to_bf16_rne(p1) << 16);
   }
   l_run += psum;
-  *(__attribute__((address_space(3))) u32x4_t*)(pout + 16 * lane) = pk;
-  if (lane < 16) *(__attribute__((address_space(3))) float*)(aout + 4 * lane) = alpha;
-}
-
-// PV wave, one tile: O^T[512 x 16 rows] = alpha * O^T + V^T[512 x 32] . P^T
-// (32 MFMA), V^T from the same LDS tile through the transposing read, kVAhead
-// blocks ahead of their MFMA.
-template <int kVAhead>
-__device__ __forceinline__ void pv_tile(f32x4v_t (&acc)[kVBlocks], lds_cchar* cur, const LaneOffsets& lo_,
-                                        lds_cchar* pin, lds_cchar* ain) {
-  const int lane = threadIdx.x & 63;
-  lds_cchar* vp[4] = {opaque_lds(cur + lo_.vbase[0]), opaque_lds(cur + lo_.vbase[1]),
-                      opaque_lds(cur + lo_.vbase[2]), opaque_lds(cur + lo_.vbase[3])};
-  auto vread = [&](int mb, int second) -> u32x2_t {
-    return __builtin_bit_cast(u32x2_t, lds_read_tr16(vp[mb & 3] + 18432 * second + 128 * (mb >> 2)));
-  };
-  u32x2_t vb[kVAhead][2];
-#pragma unroll
-  for (int m = 0; m < kVAhead; m++) {
-    vb[m][0] = vread(m, 0);
-    vb[m][1] = vread(m, 1);
-  }
-  const bf16x8_t pf = *(__attribute__((address_space(3))) const bf16x8_t*)(pin + 16 * lane);
-  const float alpha = *(__attribute__((address_space(3))) const float*)(ain + 4 * (lane & 15));
-  if (__any(alpha != 1.f)) {
-#pragma unroll
-    for (int mb = 0; mb < kVBlocks; mb++) acc[mb] *= alpha;
-  }
+  const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pk);
 #pragma unroll
   for (int mb = 0; mb < kVBlocks; mb++) {
     const u32x2_t lo = vb[mb % kVAhead][0], hi = vb[mb % kVAhead][1];
@@ -608,18 +606,10 @@ template <bool FP8>
 __device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& lo_, const Piece& pc, int w) {
   const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
   const int b = pc.b;
-  const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
-  const int tok_end = min(pc.tile1 * kTile, L);
   const int nt = pc.tile1 - pc.tile0;
   const int row = pc.rb * kRowsPerBlock + 16 * w + i16;
   const bool row_ok = row < a.R;
   const int jrow = row_ok ? row / a.H : 0, hrow = row_ok ? row - jrow * a.H : 0;
-  const int limit = min(tok_end, L - a.q_len + 1 + jrow);   // tokens t < limit are visible to this row
-  // smallest limit over the wave's rows: tiles below it need no mask
-  int lim_min = limit;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, d));
-  lim_min = __builtin_amdgcn_readfirstlane(lim_min);
   // Q^T B-operand fragments: lane holds row i16, dims 32k + 8g .. +8; rows
   // past the request's last query row load its first row and are zeroed.
   static_assert(kQSteps == 18, "load_q_fragments loads 18 fragments");
@@ -631,64 +621,63 @@ __device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
 #pragma unroll
     for (int k = 0; k < kQSteps; k++) qf[k] = __builtin_bit_cast(bf16x8_t, row_ok ? qv[k] : u32x4_t{0u, 0u, 0u, 0u});
   }
-  float m_run = kNegInf, l_run = 0.f;
   for (int j = -1; j < nt; j++) {
     lds_barrier();
     const int t = j + 1;
     if (t < nt) {
-      lds_char* pout = lds + kPBufOff + ((t & 1) * kRowGroups + w) * 1024;
-      lds_char* aout = lds + kABufOff + ((t & 1) * kRowGroups + w) * 64;
+      lds_char* sout = lds + kSBufOff + ((t & 1) * kRowGroups + w) * 2048;
       if constexpr (FP8)
-        qk_tile<MLA_F8_KA, MLA_F8_SC>(qf, m_run, l_run, lds + tile_buf(t) * kTileBytes, lo_, (pc.tile0 + t) * kTile,
-                                      limit, lim_min, a.scale_log2, pout, aout);
+        qk_tile<MLA_F8_KA, MLA_F8_SC>(qf, lds + tile_buf(t) * kTileBytes, lo_, sout);
       else
-        qk_tile<MLA_KA, MLA_SC>(qf, m_run, l_run, lds + tile_buf(t) * kTileBytes, lo_, (pc.tile0 + t) * kTile, limit,
-                                lim_min, a.scale_log2, pout, aout);
+        qk_tile<MLA_KA, MLA_SC>(qf, lds + tile_buf(t) * kTileBytes, lo_, sout);
     }
-  }
-  // the rows' final max (log2 units) and denominator for the PV waves
-  const float l_tot = row_sum4(l_run);
-  if (lane < 16) {
-    float* stats = (float*)(lds + kStatsOff);
-    stats[2 * (16 * w + i16)] = m_run;
-    stats[2 * (16 * w + i16) + 1] = l_tot;
   }
   lds_barrier();
   lds_barrier();
 }
 
-// The PV waves' side of one piece: accumulates the rows' output and writes
-// it (or the partial result) with the LSE.
+// The PV waves' side of one piece: the online softmax and the output rows,
+// written with the LSE (or as a partial result).
 template <bool FP8>
 __device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& lo_, const Piece& pc, int w) {
   const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
   const int b = pc.b;
+  const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const int tok_end = min(pc.tile1 * kTile, L);
   const int nt = pc.tile1 - pc.tile0;
+  const int rib = 16 * w + i16;   // this lane's row in the block
+  const int row = pc.rb * kRowsPerBlock + rib;
+  const int jrow = row < a.R ? row / a.H : 0;
+  const int limit = min(tok_end, L - a.q_len + 1 + jrow);   // tokens t < limit are visible to this row
+  // smallest limit over the wave's rows: tiles below it need no mask
+  int lim_min = limit;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, d));
+  lim_min = __builtin_amdgcn_readfirstlane(lim_min);
   f32x4v_t acc[kVBlocks];
 #pragma unroll
   for (int mb = 0; mb < kVBlocks; mb++) acc[mb] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
   for (int j = -1; j < nt; j++) {
     lds_barrier();
     if (j >= 0) {
-      lds_cchar* pin = lds + kPBufOff + ((j & 1) * kRowGroups + w) * 1024;
-      lds_cchar* ain = lds + kABufOff + ((j & 1) * kRowGroups + w) * 64;
+      lds_cchar* sin = lds + kSBufOff + ((j & 1) * kRowGroups + w) * 2048;
       if constexpr (FP8)
-        pv_tile<MLA_F8_VA>(acc, lds + tile_buf(j) * kTileBytes, lo_, pin, ain);
+        pv_tile<MLA_F8_VA>(acc, m_run, l_run, lds + tile_buf(j) * kTileBytes, lo_, sin, (pc.tile0 + j) * kTile,
+                           limit, lim_min, a.scale_log2);
       else
-        pv_tile<MLA_VA>(acc, lds + tile_buf(j) * kTileBytes, lo_, pin, ain);
+        pv_tile<MLA_VA>(acc, m_run, l_run, lds + tile_buf(j) * kTileBytes, lo_, sin, (pc.tile0 + j) * kTile, limit,
+                        lim_min, a.scale_log2);
     }
   }
-  lds_barrier();   // every tile is done; the QK waves' row statistics are in LDS
+  lds_barrier();   // every tile is done
 
   // ---- epilogue.  The bf16 rows are staged in LDS (the tile buffers) so
   // that every output row leaves as one contiguous 1 KB store of a wave
   // instead of 16 rows x 32 bytes per store.
   constexpr int kStagePitch = kLatentDim * 2 + 16;   // rows 16 bytes apart in the banks
   static_assert(kRowsPerBlock * kStagePitch <= kTileBufs * kTileBytes, "staged rows fit the tile buffers");
-  const int rib = 16 * w + i16;   // this lane's row in the block
-  const int row = pc.rb * kRowsPerBlock + rib;
-  const float* stats = (const float*)(lds + kStatsOff);
-  const float m_run = stats[2 * rib], l_tot = stats[2 * rib + 1];
+  const float l_tot = row_sum4(l_run);
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : a.out_scale / l_tot;
   const float lse_nat = empty ? kNegInf : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
@@ -731,9 +720,10 @@ __device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
 }
 
 // Block-wide computation of unit_off[0..B] into LDS (balanced mode).
+// part: NT ints of LDS scratch.
 template <int NT>
-__device__ void build_unit_offsets(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t* off) {
-  __shared__ int32_t part[NT];
+__device__ void build_unit_offsets(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t* off,
+                                   int32_t* part) {
   const int tid = threadIdx.x;
   const int per = (B + NT - 1) / NT;
   const int b0 = tid * per, b1 = min(B, b0 + per);
@@ -795,7 +785,7 @@ __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a
   int32_t total = 0, b_first = 0, off_first = 0;
   if (a.num_splits == 0) {
     int32_t* off = (int32_t*)smem;
-    build_unit_offsets<kSplitThreads>(a.seq_lens, a.B, a.max_seq_len, off);
+    build_unit_offsets<kSplitThreads>(a.seq_lens, a.B, a.max_seq_len, off, off + kMaxBatch + 1);
     if (blockIdx.x == 0)
       for (int b = threadIdx.x; b <= a.B; b += kSplitThreads) a.unit_off_ws[b] = off[b];
     total = __builtin_amdgcn_readfirstlane(off[a.B]);
@@ -991,7 +981,8 @@ __global__ __launch_bounds__(kThreads) void mla_plan_kernel(const int32_t* seq_l
     }
     n++;
   };
-  if (num_splits == 0) build_unit_offsets<kThreads>(seq_lens, B, max_seq_len, off);
+  __shared__ int32_t part[kThreads];
+  if (num_splits == 0) build_unit_offsets<kThreads>(seq_lens, B, max_seq_len, off, part);
   if (grp >= NG) return;
   if (num_splits > 0) {
     const int32_t b = (int32_t)(grp / num_splits);
