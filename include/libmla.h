@@ -33,7 +33,8 @@
  *    lie in [0, max_seq_len] (values outside are clamped), and every
  *    block-table entry a request reads (index < ceil(seq_lens[b] /
  *    page_size)) must lie in [0, num_pages).  An entry outside that range is
- *    never dereferenced (that tile is skipped, and the result is undefined).  Entries past a request's
+ *    never dereferenced: a bf16 pool reads page 0 in its place, an fp8 pool
+ *    reads zeros, and the result is undefined.  Entries past a request's
  *    last page are never read and may hold anything (-1, 0, ...).
  *    mla_check_inputs_host() checks all of this on host copies.
  *  - A workspace must not be shared by calls that may run concurrently.

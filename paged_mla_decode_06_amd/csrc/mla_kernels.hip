@@ -48,19 +48,19 @@ constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
 #define MLA_KA 6
 #endif
 #ifndef MLA_VA
-#define MLA_VA 2
+#define MLA_VA 1
 #endif
 #ifndef MLA_SC
-#define MLA_SC 2
+#define MLA_SC 4
 #endif
 #ifndef MLA_F8_KA
 #define MLA_F8_KA 8
 #endif
 #ifndef MLA_F8_VA
-#define MLA_F8_VA 4
+#define MLA_F8_VA 1
 #endif
 #ifndef MLA_F8_SC
-#define MLA_F8_SC 2
+#define MLA_F8_SC 4
 #endif
 constexpr int kRowsPerWave = 16 * kRowBlocksPerWave;
 static_assert(kRowBlocksPerWave == 1, "one 16-row MFMA block per wave");
@@ -100,11 +100,14 @@ static_assert(kChunks % 64 == 0, "tile must be a whole number of wave-wide loads
 static_assert(kTileLoads % kLoaderWaves == 0, "every loader wave issues the same number of tile loads");
 // KV tile buffers in LDS: kTileBufs - 1 tiles are in flight while one is consumed.
 constexpr int kTileBufs = 4;
-// LDS of a split workgroup: the tile ring, then two sets of score tiles
-// (one 2 KB block per QK wave: its lanes' 8 fp32 scores) -- 160 KB in all,
-// the whole LDS of a gfx950 workgroup, so the kernel has no static LDS.
-constexpr int kSBufOff = kTileBufs * kTileBytes;
-constexpr int kSplitLdsBytes = kSBufOff + 2 * kRowGroups * 2048;
+// LDS of a split workgroup: the tile ring; two sets (by tile parity) of the
+// softmax weights P (one 1 KB block per row group: its lanes' MFMA operands)
+// and of the per-row rescale factors; the final row statistics.  The kernel
+// has no static LDS.
+constexpr int kPBufOff = kTileBufs * kTileBytes;
+constexpr int kABufOff = kPBufOff + 2 * kRowGroups * 1024;
+constexpr int kStatsOff = kABufOff + 2 * kRowsPerBlock * 4;
+constexpr int kSplitLdsBytes = kStatsOff + kRowsPerBlock * 8;
 static_assert(kSplitLdsBytes <= 160 * 1024, "split workgroup LDS");
 static_assert((kMaxBatch + 1 + 1024) * 4 <= kTileBufs * kTileBytes, "planning scan scratch fits the tile buffers");
 static_assert(kTile == 32, "the MFMA layout below assumes 32-token tiles");
@@ -273,16 +276,17 @@ struct Stage<false> {
   // Issues exactly kLoadsPerWave loads per loader wave for a tile that holds
   // at least one valid token (the waits below count on it); rows past the
   // last valid token re-read the same chunk of the tile's first row, so every
-  // LDS row stays finite.  A tile with no valid token (only a request with no
-  // token at all) or a block-table entry outside [0, N) issues nothing.
+  // LDS row stays finite.  A block-table entry outside [0, N) reads page 0 in
+  // its place (the result is undefined then, but the count holds).  A tile
+  // with no valid token (only a request with no token at all) issues nothing.
   // Called by loader wave lw; returns the number of loads it issued (0 or kLoadsPerWave).
   __device__ __forceinline__ int issue(const SplitArgs& a, lds_char* buf, PageWindow& pw, int b, int ts,
                                        int tok_end, int lw) const {
     const int wave = lw;
     if (ts >= tok_end) return 0;
     const int32_t page = pw.page(a, b, ts / a.P);
-    if ((uint32_t)page >= (uint32_t)a.N) return 0;
-    const char* base = (const char*)a.pool + ((int64_t)page * a.P + (ts % a.P)) * (int64_t)kRowBytes;
+    const int32_t pg = (uint32_t)page < (uint32_t)a.N ? page : 0;
+    const char* base = (const char*)a.pool + ((int64_t)pg * a.P + (ts % a.P)) * (int64_t)kRowBytes;
     const uint32_t dst = (uint32_t)(uintptr_t)(buf + wave * 1024);
     // Opaque copies: the offsets are unpacked here, once per tile, instead of
     // being hoisted out of the tile loop as nine live registers.
@@ -306,7 +310,8 @@ struct Stage<false> {
     }
     return kLoadsPerWave;
   }
-  // Wait until at most `later` tiles' loads (issued after this tile's) are in flight.
+  // Wait until this tile's loads have landed while the loads of `later`
+  // tiles issued after it may stay in flight (loads complete in issue order).
   __device__ __forceinline__ void wait(int later) const {
     static_assert(kLoadsPerWave == 9, "the vmcnt immediates assume 9 loads per loader wave and tile");
     if (later >= 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
@@ -412,6 +417,23 @@ __device__ __forceinline__ lds_cchar* opaque_lds(lds_cchar* p) {
 #ifndef MLA_PIN_ORDER
 #define MLA_PIN_ORDER 1
 #endif
+// Issue priorities of the QK and loader waves (the PV waves keep 0).
+#ifndef MLA_PRIO_QK
+#define MLA_PRIO_QK 1
+#endif
+#ifndef MLA_PRIO_LD
+#define MLA_PRIO_LD 3
+#endif
+// Row groups per PV wave.  The kRowGroups PV waves split the (row group,
+// 16-dim block) grid: kPVRowGroups row groups times 1/kPVRowGroups of the 32
+// dim blocks each, so a V^T fragment read from LDS feeds kPVRowGroups MFMAs.
+#ifndef MLA_PV_RG
+#define MLA_PV_RG 2
+#endif
+constexpr int kPVRowGroups = MLA_PV_RG;
+constexpr int kPVDimParts = kPVRowGroups;           // dim ranges per row group
+constexpr int kPVBlocks = kVBlocks / kPVDimParts;   // 16-dim blocks of one PV wave
+static_assert(kRowGroups % kPVRowGroups == 0 && kPVBlocks % 4 == 0, "PV work split");
 __device__ __forceinline__ s16x4_t lds_read_tr16(lds_cchar* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
 }
@@ -448,14 +470,13 @@ struct LaneOffsets {
 };
 
 // QK wave, one tile: S^T[32 tokens x 16 rows] = K_tile . Q^T (36 MFMA), the
-// K reads kKAhead steps ahead of their MFMA; the lane's 8 fp32 scores (token
-// 4g + r and 16 + 4g + r of row l%16) go to LDS for the PV wave of the rows.
+// K reads kKAhead steps ahead of their MFMA.  Lane l ends with the scores of
+// row l%16 for tokens 4g + r (s0[r]) and 16 + 4g + r (s1[r]), g = l/16.
 template <int kKAhead, int kSChains>
 __device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[kQSteps], lds_cchar* cur, const LaneOffsets& lo_,
-                                        lds_char* sout) {
+                                        f32x4v_t& s0, f32x4v_t& s1) {
   static_assert(kSChains == 2 || kSChains == 4, "one or two accumulation chains per token block");
   constexpr int kCh = kSChains / 2;
-  const int lane = threadIdx.x & 63;
   lds_cchar* kp[2] = {opaque_lds(cur + lo_.kbase[0]), opaque_lds(cur + lo_.kbase[1])};
   auto kread = [&](int s) -> bf16x8_t {
     const int k = s >> 1, tb = s & 1;
@@ -479,46 +500,28 @@ __device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[kQSteps], lds_cchar
     // scheduler sinks the reads next to their use and exposes the LDS latency
     if (MLA_PIN_ORDER) __builtin_amdgcn_sched_barrier(0);
   }
-  f32x4v_t s0 = sp[0][0], s1 = sp[1][0];
+  s0 = sp[0][0];
+  s1 = sp[1][0];
   if constexpr (kCh == 2) {
     s0 += sp[0][1];
     s1 += sp[1][1];
   }
-  *(__attribute__((address_space(3))) f32x4v_t*)(sout + 32 * lane) = s0;
-  *(__attribute__((address_space(3))) f32x4v_t*)(sout + 32 * lane + 16) = s1;
 }
 
-// PV wave, one tile: the online softmax of the lane's 8 scores of its row
-// (read from the QK wave's block), then O^T[512 x 16 rows] = alpha * O^T +
-// V^T[512 x 32] . P^T (32 MFMA), V^T from the same LDS tile through the
-// transposing read, kVAhead blocks ahead of their MFMA.  Running the softmax
-// here lets it overlap the QK wave's MFMAs of the next tile.
-template <int kVAhead>
-__device__ __forceinline__ void pv_tile(f32x4v_t (&acc)[kVBlocks], float& m_run, float& l_run, lds_cchar* cur,
-                                        const LaneOffsets& lo_, lds_cchar* sin, int ts, int limit, int lim_min,
-                                        float scale_log2) {
+// QK wave, one tile: the online softmax of the lane's 8 scores of its row.
+// The bf16 weights go to LDS as the lane's 16-byte B operand of the PV MFMA
+// (tokens in the order of the scores: the V^T reads follow the same order),
+// and the factor by which the row's running output is to be rescaled.
+__device__ __forceinline__ void softmax_tile(f32x4v_t s0, f32x4v_t s1, float& m_run, float& l_run, int ts, int limit,
+                                             int lim_min, float scale_log2, lds_char* pout, lds_char* aout) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
-  lds_cchar* vp[4] = {opaque_lds(cur + lo_.vbase[0]), opaque_lds(cur + lo_.vbase[1]),
-                      opaque_lds(cur + lo_.vbase[2]), opaque_lds(cur + lo_.vbase[3])};
-  auto vread = [&](int mb, int second) -> u32x2_t {
-    return __builtin_bit_cast(u32x2_t, lds_read_tr16(vp[mb & 3] + 18432 * second + 128 * (mb >> 2)));
-  };
-  const f32x4v_t s0 = *(__attribute__((address_space(3))) const f32x4v_t*)(sin + 32 * lane);
-  const f32x4v_t s1 = *(__attribute__((address_space(3))) const f32x4v_t*)(sin + 32 * lane + 16);
-  u32x2_t vb[kVAhead][2];
-#pragma unroll
-  for (int m = 0; m < kVAhead; m++) {
-    vb[m][0] = vread(m, 0);
-    vb[m][1] = vread(m, 1);
-  }
-  // every token of the tile is visible to every row of the wave: no mask
-  const bool masked = ts + kTile > lim_min;
-  // raw scores of the lane's 8 tokens; masked tokens become -inf
+  // raw scores of the lane's 8 tokens; masked tokens become -inf (a tile
+  // below lim_min is visible to every row of the wave)
   float sv[8];
 #pragma unroll
   for (int e = 0; e < 8; e++) sv[e] = e < 4 ? s0[e & 3] : s1[e & 3];
-  if (masked) {
+  if (ts + kTile > lim_min) {
 #pragma unroll
     for (int e = 0; e < 8; e++) {
       const int t = ts + 16 * (e >> 2) + 4 * g + (e & 3);
@@ -531,12 +534,11 @@ __device__ __forceinline__ void pv_tile(f32x4v_t (&acc)[kVBlocks], float& m_run,
   float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
   mx = row_max4(mx) * scale_log2;
   const bool need = mx > m_run + kRescaleSlack;
+  float alpha = 1.f;
   if (__any(need)) {
     const float m_new = need ? mx : m_run;
-    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // m_run = -inf gives 0
+    alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // m_run = -inf gives 0
     l_run *= alpha;
-#pragma unroll
-    for (int mb = 0; mb < kVBlocks; mb++) acc[mb] *= alpha;
     m_run = m_new;
   }
   const float m_use = m_run == kNegInf ? 0.f : m_run;
@@ -550,16 +552,62 @@ __device__ __forceinline__ void pv_tile(f32x4v_t (&acc)[kVBlocks], float& m_run,
     pk[e] = (uint32_t)f32_to_bf16_rne(p0) | ((uint32_t)f32_to_bf16_rne(p1) << 16);
   }
   l_run += psum;
-  const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pk);
+  *(__attribute__((address_space(3))) u32x4_t*)(pout + 16 * lane) = pk;
+  if (g == 0) *(__attribute__((address_space(3))) float*)aout = alpha;
+}
+
+// PV wave, one tile: for its kPVRowGroups row groups and kPVBlocks dim
+// blocks, O^T = alpha * O^T + V^T[16 dims x 32] . P^T (kPVRowGroups MFMA per
+// block), V^T from the LDS tile through the transposing read, kVAhead blocks
+// ahead of their MFMAs.  vcur is the tile plus the wave's first dim block.
+template <int kVAhead>
+__device__ __forceinline__ void pv_tile(f32x4v_t (&acc)[kPVRowGroups][kPVBlocks], lds_cchar* vcur,
+                                        const LaneOffsets& lo_, lds_cchar* pin, lds_cchar* ain) {
+  const int lane = threadIdx.x & 63;
+  lds_cchar* vp[4] = {opaque_lds(vcur + lo_.vbase[0]), opaque_lds(vcur + lo_.vbase[1]),
+                      opaque_lds(vcur + lo_.vbase[2]), opaque_lds(vcur + lo_.vbase[3])};
+  auto vread = [&](int mb, int second) -> u32x2_t {
+    return __builtin_bit_cast(u32x2_t, lds_read_tr16(vp[mb & 3] + 18432 * second + 128 * (mb >> 2)));
+  };
+  u32x2_t vb[kVAhead][2];
 #pragma unroll
-  for (int mb = 0; mb < kVBlocks; mb++) {
+  for (int m = 0; m < kVAhead; m++) {
+    vb[m][0] = vread(m, 0);
+    vb[m][1] = vread(m, 1);
+  }
+  bf16x8_t pf[kPVRowGroups];
+#pragma unroll
+  for (int r = 0; r < kPVRowGroups; r++)
+    pf[r] = *(__attribute__((address_space(3))) const bf16x8_t*)(pin + 1024 * r + 16 * lane);
+  float alpha[kPVRowGroups];
+  if constexpr (kPVRowGroups == 4) {
+    const f32x4v_t a4 = *(__attribute__((address_space(3))) const f32x4v_t*)ain;
+#pragma unroll
+    for (int r = 0; r < 4; r++) alpha[r] = a4[r];
+  } else {
+#pragma unroll
+    for (int r = 0; r < kPVRowGroups; r++) alpha[r] = ((__attribute__((address_space(3))) const float*)ain)[r];
+  }
+  bool any = false;
+#pragma unroll
+  for (int r = 0; r < kPVRowGroups; r++) any |= alpha[r] != 1.f;
+  if (__any(any)) {
+#pragma unroll
+    for (int r = 0; r < kPVRowGroups; r++)
+#pragma unroll
+      for (int mb = 0; mb < kPVBlocks; mb++) acc[r][mb] *= alpha[r];
+  }
+#pragma unroll
+  for (int mb = 0; mb < kPVBlocks; mb++) {
     const u32x2_t lo = vb[mb % kVAhead][0], hi = vb[mb % kVAhead][1];
-    if (mb + kVAhead < kVBlocks) {
+    if (mb + kVAhead < kPVBlocks) {
       vb[mb % kVAhead][0] = vread(mb + kVAhead, 0);
       vb[mb % kVAhead][1] = vread(mb + kVAhead, 1);
     }
     const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[mb], 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < kPVRowGroups; r++)
+      acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[r], acc[r][mb], 0, 0, 0);
     if (MLA_PIN_ORDER) __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -567,10 +615,11 @@ __device__ __forceinline__ void pv_tile(f32x4v_t (&acc)[kVBlocks], float& m_run,
 // The pipeline of one piece runs in intervals j = -1 .. nt-1, each opened by
 // a workgroup barrier; in interval j the QK waves take tile j+1, the PV waves
 // tile j, and the loaders issue tile j+3 into the buffer of tile j-1 (free:
-// the PV waves finished it in interval j-1, the QK waves in j-2).  Two more
-// barriers close the piece: after the first the QK waves' final row max and
-// sum are in LDS and every tile is done; after the second the PV waves have
-// read the output rows they staged in the tile buffers.
+// the PV waves finished it in interval j-1, the QK waves in j-2).  Three
+// more barriers close the piece: after the first every tile is done and the
+// QK waves' final row max and sum are in LDS; after the second the PV waves
+// have staged the output rows in the tile buffers; after the third those
+// rows have been copied out.
 __device__ __forceinline__ int tile_buf(int t) { return t & (kTileBufs - 1); }
 static_assert((kTileBufs & (kTileBufs - 1)) == 0, "tile_buf masks the tile index");
 
@@ -599,17 +648,28 @@ __device__ void load_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, c
   }
   lds_barrier();
   lds_barrier();
+  lds_barrier();
 }
 
-// The QK waves' side of one piece.
+// The QK waves' side of one piece: the scores and the online softmax of the
+// wave's 16 rows.
 template <bool FP8>
 __device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& lo_, const Piece& pc, int w) {
   const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
   const int b = pc.b;
+  const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const int tok_end = min(pc.tile1 * kTile, L);
   const int nt = pc.tile1 - pc.tile0;
-  const int row = pc.rb * kRowsPerBlock + 16 * w + i16;
+  const int rib = 16 * w + i16;   // this lane's row in the block
+  const int row = pc.rb * kRowsPerBlock + rib;
   const bool row_ok = row < a.R;
   const int jrow = row_ok ? row / a.H : 0, hrow = row_ok ? row - jrow * a.H : 0;
+  const int limit = min(tok_end, L - a.q_len + 1 + jrow);   // tokens t < limit are visible to this row
+  // smallest limit over the wave's rows: tiles below it need no mask
+  int lim_min = limit;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, d));
+  lim_min = __builtin_amdgcn_readfirstlane(lim_min);
   // Q^T B-operand fragments: lane holds row i16, dims 32k + 8g .. +8; rows
   // past the request's last query row load its first row and are zeroed.
   static_assert(kQSteps == 18, "load_q_fragments loads 18 fragments");
@@ -621,92 +681,105 @@ __device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
 #pragma unroll
     for (int k = 0; k < kQSteps; k++) qf[k] = __builtin_bit_cast(bf16x8_t, row_ok ? qv[k] : u32x4_t{0u, 0u, 0u, 0u});
   }
+  float m_run = kNegInf, l_run = 0.f;
   for (int j = -1; j < nt; j++) {
     lds_barrier();
     const int t = j + 1;
     if (t < nt) {
-      lds_char* sout = lds + kSBufOff + ((t & 1) * kRowGroups + w) * 2048;
+      f32x4v_t s0, s1;
       if constexpr (FP8)
-        qk_tile<MLA_F8_KA, MLA_F8_SC>(qf, lds + tile_buf(t) * kTileBytes, lo_, sout);
+        qk_tile<MLA_F8_KA, MLA_F8_SC>(qf, lds + tile_buf(t) * kTileBytes, lo_, s0, s1);
       else
-        qk_tile<MLA_KA, MLA_SC>(qf, lds + tile_buf(t) * kTileBytes, lo_, sout);
+        qk_tile<MLA_KA, MLA_SC>(qf, lds + tile_buf(t) * kTileBytes, lo_, s0, s1);
+      softmax_tile(s0, s1, m_run, l_run, (pc.tile0 + t) * kTile, limit, lim_min, a.scale_log2,
+                   lds + kPBufOff + ((t & 1) * kRowGroups + w) * 1024,
+                   lds + kABufOff + (t & 1) * (kRowsPerBlock * 4) + 16 * i16 + 4 * w);
     }
   }
+  const float l_tot = row_sum4(l_run);
+  if (g == 0) {
+    float* stats = (float*)(lds + kStatsOff);
+    stats[2 * rib] = m_run;
+    stats[2 * rib + 1] = l_tot;
+  }
+  lds_barrier();
   lds_barrier();
   lds_barrier();
 }
 
-// The PV waves' side of one piece: the online softmax and the output rows,
-// written with the LSE (or as a partial result).
+// The PV waves' side of one piece: the output rows, written with the LSE (or
+// as a partial result).
 template <bool FP8>
-__device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& lo_, const Piece& pc, int w) {
+__device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& lo_, const Piece& pc, int v) {
   const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
   const int b = pc.b;
-  const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
-  const int tok_end = min(pc.tile1 * kTile, L);
   const int nt = pc.tile1 - pc.tile0;
-  const int rib = 16 * w + i16;   // this lane's row in the block
-  const int row = pc.rb * kRowsPerBlock + rib;
-  const int jrow = row < a.R ? row / a.H : 0;
-  const int limit = min(tok_end, L - a.q_len + 1 + jrow);   // tokens t < limit are visible to this row
-  // smallest limit over the wave's rows: tiles below it need no mask
-  int lim_min = limit;
+  const int rg0 = kPVRowGroups * (v / kPVDimParts);   // first row group of this wave
+  const int mb0 = kPVBlocks * (v % kPVDimParts);      // first 16-dim block of this wave
+  f32x4v_t acc[kPVRowGroups][kPVBlocks];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, d));
-  lim_min = __builtin_amdgcn_readfirstlane(lim_min);
-  f32x4v_t acc[kVBlocks];
+  for (int r = 0; r < kPVRowGroups; r++)
 #pragma unroll
-  for (int mb = 0; mb < kVBlocks; mb++) acc[mb] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
+    for (int mb = 0; mb < kPVBlocks; mb++) acc[r][mb] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
   for (int j = -1; j < nt; j++) {
     lds_barrier();
     if (j >= 0) {
-      lds_cchar* sin = lds + kSBufOff + ((j & 1) * kRowGroups + w) * 2048;
+      lds_cchar* vcur = lds + tile_buf(j) * kTileBytes + 32 * mb0;
+      lds_cchar* pin = lds + kPBufOff + ((j & 1) * kRowGroups + rg0) * 1024;
+      lds_cchar* ain = lds + kABufOff + (j & 1) * (kRowsPerBlock * 4) + 16 * i16 + 4 * rg0;
       if constexpr (FP8)
-        pv_tile<MLA_F8_VA>(acc, m_run, l_run, lds + tile_buf(j) * kTileBytes, lo_, sin, (pc.tile0 + j) * kTile,
-                           limit, lim_min, a.scale_log2);
+        pv_tile<MLA_F8_VA>(acc, vcur, lo_, pin, ain);
       else
-        pv_tile<MLA_VA>(acc, m_run, l_run, lds + tile_buf(j) * kTileBytes, lo_, sin, (pc.tile0 + j) * kTile, limit,
-                        lim_min, a.scale_log2);
+        pv_tile<MLA_VA>(acc, vcur, lo_, pin, ain);
     }
   }
-  lds_barrier();   // every tile is done
+  lds_barrier();   // every tile is done; the QK waves' row statistics are in LDS
 
   // ---- epilogue.  The bf16 rows are staged in LDS (the tile buffers) so
   // that every output row leaves as one contiguous 1 KB store of a wave
   // instead of 16 rows x 32 bytes per store.
   constexpr int kStagePitch = kLatentDim * 2 + 16;   // rows 16 bytes apart in the banks
   static_assert(kRowsPerBlock * kStagePitch <= kTileBufs * kTileBytes, "staged rows fit the tile buffers");
-  const float l_tot = row_sum4(l_run);
-  const bool empty = !(l_tot > 0.f);
-  const float inv = empty ? 0.f : a.out_scale / l_tot;
-  const float lse_nat = empty ? kNegInf : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-  lds_char* srow = lds + rib * kStagePitch + 8 * g;
+  const float* stats = (const float*)(lds + kStatsOff);
 #pragma unroll
-  for (int mb = 0; mb < kVBlocks; mb++) {
-    const f32x4v_t v = acc[mb] * inv;
-    u32x2_t wv;
-    wv[0] = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-    wv[1] = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-    *(__attribute__((address_space(3))) u32x2_t*)(srow + 32 * mb) = wv;
-  }
-  if (row < a.R && g == 0) {
-    if (pc.slot < 0) {
-      if (a.lse != nullptr) {
-        const int jq = row / a.H;
-        a.lse[(int64_t)(b * a.q_len + jq) * a.H + (row - jq * a.H)] = lse_nat;
-      }
-    } else {
-      a.part_lse[(int64_t)pc.slot * kRowsPerBlock + rib] = lse_nat;
+  for (int r = 0; r < kPVRowGroups; r++) {
+    const int rib = 16 * (rg0 + r) + i16;
+    const float l_tot = stats[2 * rib + 1];
+    const float inv = l_tot > 0.f ? a.out_scale / l_tot : 0.f;
+    lds_char* srow = lds + rib * kStagePitch + 32 * mb0 + 8 * g;
+#pragma unroll
+    for (int mb = 0; mb < kPVBlocks; mb++) {
+      const f32x4v_t o = acc[r][mb] * inv;
+      u32x2_t wv;
+      wv[0] = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+      wv[1] = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+      *(__attribute__((address_space(3))) u32x2_t*)(srow + 32 * mb) = wv;
     }
   }
-  // A wave copies out the rows it staged (its own LDS writes are ordered
-  // before its reads): lane l carries bytes 16l .. 16l+15 of the row.
+  lds_barrier();   // every row is staged
+  // Wave v copies out rows 16v .. 16v+15 and their LSEs: lane l carries bytes
+  // 16l .. 16l+15 of a row.
+  {
+    const int rib = 16 * v + i16;
+    const int row = pc.rb * kRowsPerBlock + rib;
+    if (row < a.R && g == 0) {
+      const float m_run = stats[2 * rib], l_tot = stats[2 * rib + 1];
+      const float lse_nat = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+      if (pc.slot < 0) {
+        if (a.lse != nullptr) {
+          const int jq = row / a.H;
+          a.lse[(int64_t)(b * a.q_len + jq) * a.H + (row - jq * a.H)] = lse_nat;
+        }
+      } else {
+        a.part_lse[(int64_t)pc.slot * kRowsPerBlock + rib] = lse_nat;
+      }
+    }
+  }
   for (int rr = 0; rr < 16; rr++) {
-    const int r_in = 16 * w + rr;
+    const int r_in = 16 * v + rr;
     const int r = pc.rb * kRowsPerBlock + r_in;
     if (r >= a.R) break;
-    const u32x4_t v = *(__attribute__((address_space(3))) const u32x4_t*)(lds + r_in * kStagePitch + 16 * lane);
+    const u32x4_t o = *(__attribute__((address_space(3))) const u32x4_t*)(lds + r_in * kStagePitch + 16 * lane);
     uint16_t* dst;
     if (pc.slot < 0) {
       const int jq = r / a.H;
@@ -714,7 +787,7 @@ __device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
     } else {
       dst = a.part_o + ((int64_t)pc.slot * kRowsPerBlock + r_in) * kLatentDim;
     }
-    *(u32x4_t*)(dst + 8 * lane) = v;
+    *(u32x4_t*)(dst + 8 * lane) = o;
   }
   lds_barrier();   // every wave has read its rows before the next piece's tile loads land there
 }
@@ -803,6 +876,7 @@ __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a
   if (grp >= a.NG) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave >= kLoaderWave0) {
+    if (MLA_PRIO_LD) __builtin_amdgcn_s_setprio(MLA_PRIO_LD);
     const int lw = wave - kLoaderWave0;
     Stage<FP8> stg;
     stg.init(lw);
@@ -814,6 +888,7 @@ __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a
     for_each_piece<FP8>(a, grp, rb, total, b_first, off_first,
                         [&](const Piece& pc) { pv_piece<FP8>(a, tiles, lo_, pc, wave - kPVWave0); });
   } else {
+    if (MLA_PRIO_QK) __builtin_amdgcn_s_setprio(MLA_PRIO_QK);
     LaneOffsets lo_;
     lo_.init();
     for_each_piece<FP8>(a, grp, rb, total, b_first, off_first,

@@ -84,37 +84,54 @@ struct Piece {
   int32_t b, rb, tile0, tile1, slot;
 };
 
-// Pieces of balanced-mode group g for row block rb.  total is the number of
-// units of all requests; b_first is the request holding the group's first
-// unit start(g) (off(b_first) <= start(g) < off(b_first + 1), off(b) = sum of
-// U_b' for b' < b) and off_first = off(b_first); units(b) returns U_b.  The
+// Pieces of balanced-mode group g for row block rb, one at a time.  total is
+// the number of units of all requests; b_first is the request holding the
+// group's first unit start(g) (off(b_first) <= start(g) < off(b_first + 1),
+// off(b) = sum of U_b' for b' < b) and off_first = off(b_first).  The
 // requests of the share are walked in order, so no table of offsets is
-// needed.  fn(Piece) is called for each piece in order.
-template <class Units, class Fn>
-MLA_HD void balanced_pieces(int64_t g, int64_t G, int32_t rb, int32_t nrb, int64_t total, int32_t b_first,
-                            int64_t off_first, const Units& units, Fn&& fn) {
-  const int64_t u_begin = wg_start(g, total, G), u_end = wg_start(g + 1, total, G);
-  if (u_begin >= u_end) return;
-  const int64_t wg = g * nrb + rb;
-  int32_t b = b_first;
-  int64_t ob = off_first;
-  int64_t u = u_begin;
-  while (u < u_end) {
+// needed; next(units, &pc) yields the following piece (units(b) returns U_b)
+// or false after the last.
+struct BalancedWalk {
+  int64_t u, u_begin, u_end, ob, wg;
+  int32_t b, rb;
+  MLA_HD void init(int64_t g, int64_t G, int32_t rb_, int32_t nrb, int64_t total, int32_t b_first,
+                   int64_t off_first) {
+    u_begin = wg_start(g, total, G);
+    u_end = wg_start(g + 1, total, G);
+    u = u_begin;
+    ob = off_first;
+    wg = g * nrb + rb_;
+    b = b_first;
+    rb = rb_;
+  }
+  template <class Units>
+  MLA_HD bool next(const Units& units, Piece* pc) {
+    if (u >= u_end) return false;
     const int32_t U = units(b);
     const int64_t oe = ob + U;
     const int64_t pe = oe < u_end ? oe : u_end;
-    Piece pc;
-    pc.b = b;
-    pc.rb = rb;
-    pc.tile0 = (int32_t)(u - ob);
-    pc.tile1 = (int32_t)(pe - ob);
-    const bool whole = pc.tile0 == 0 && pc.tile1 == U;
-    pc.slot = whole ? -1 : (int32_t)(2 * wg + (u == u_begin ? 0 : 1));
-    fn(pc);
+    pc->b = b;
+    pc->rb = rb;
+    pc->tile0 = (int32_t)(u - ob);
+    pc->tile1 = (int32_t)(pe - ob);
+    const bool whole = pc->tile0 == 0 && pc->tile1 == U;
+    pc->slot = whole ? -1 : (int32_t)(2 * wg + (u == u_begin ? 0 : 1));
     u = pe;
     ob = oe;
     b++;
+    return true;
   }
+};
+
+// All pieces of balanced-mode group g for row block rb: fn(Piece) is called
+// for each in order.
+template <class Units, class Fn>
+MLA_HD void balanced_pieces(int64_t g, int64_t G, int32_t rb, int32_t nrb, int64_t total, int32_t b_first,
+                            int64_t off_first, const Units& units, Fn&& fn) {
+  BalancedWalk w;
+  w.init(g, G, rb, nrb, total, b_first, off_first);
+  Piece pc;
+  while (w.next(units, &pc)) fn(pc);
 }
 
 // The single piece of forced-mode group g for row block rb, or false.  U is

@@ -43,8 +43,9 @@ def compare(o, l, ref_o, ref_l, fp8=False, what=""):
     assert np.isfinite(o).all(), f"{what}: non-finite output"
     scale = float(np.max(np.abs(ref_o))) if ref_o.size else 0.0
     err = float(np.max(np.abs(o - ref_o))) if ref_o.size else 0.0
-    assert err <= tol * max(scale, 1e-30) or (scale == 0 and err == 0), \
-        f"{what}: max|gpu-oracle| = {err:.3e} > {tol} * {scale:.3e}"
+    if not (err <= tol * max(scale, 1e-30) or (scale == 0 and err == 0)):
+        raise AssertionError(f"{what}: max|gpu-oracle| = {err:.3e} > {tol} * {scale:.3e}\n" +
+                             _mismatch_report(o, l, ref_o, ref_l, tol * max(scale, 1e-30)))
     if l is not None:
         ref_l = np.asarray(ref_l)
         inf = np.isneginf(ref_l)
@@ -53,3 +54,23 @@ def compare(o, l, ref_o, ref_l, fp8=False, what=""):
             lerr = float(np.max(np.abs(l[~inf] - ref_l[~inf])))
             assert lerr <= LSE_TOL, f"{what}: max|lse err| = {lerr:.3e}"
     return err / max(scale, 1e-30)
+
+
+def _mismatch_report(o, l, ref_o, ref_l, bound):
+    """Where the output is off: per (request, query position) the rows over
+    the bound and the span of dims involved, and the LSE error there."""
+    d = np.abs(o - ref_o)
+    bad = d > bound
+    lines = []
+    B, ql, H, _ = o.shape
+    for b in range(B):
+        for j in range(ql):
+            rows = np.nonzero(bad[b, j].any(axis=-1))[0]
+            if rows.size == 0:
+                continue
+            dims = np.nonzero(bad[b, j].any(axis=0))[0]
+            lse_err = (float(np.nanmax(np.abs(np.asarray(l)[b, j, rows] - np.asarray(ref_l)[b, j, rows])))
+                       if l is not None else float("nan"))
+            lines.append(f"  b={b} j={j}: {rows.size} rows in [{rows.min()}, {rows.max()}], dims [{dims.min()}, "
+                         f"{dims.max()}] ({dims.size}), max err {d[b, j].max():.3e}, lse err there {lse_err:.2e}")
+    return "\n".join(lines[:40])
