@@ -136,8 +136,9 @@ def copy_calibration(nbytes: int, reps: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps first; a few hundred let the GPU clocks settle")
     ap.add_argument("--workload", default="deepseek_decode")
     ap.add_argument("--rotate-gib", type=float, default=1.5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
