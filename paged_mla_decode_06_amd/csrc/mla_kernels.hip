@@ -176,8 +176,14 @@ __device__ __forceinline__ void load_q_fragments(u32x4_t (&q)[18], const void* p
 // through LDS alone (tile loads are awaited explicitly with vmcnt before the
 // barrier), so the barrier must not wait for the global loads in flight: a
 // full __syncthreads would drain the tile prefetches at every tile.
+// The explicit lgkmcnt(0) makes this wave's own LDS writes complete before it
+// arrives: the workgroup fence restricted to LDS emits no wait on gfx950, and
+// without one a write issued just before the barrier (the softmax weights, a
+// staged output row) could still be in flight when a wave on another SIMD
+// passes the barrier and reads it.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
@@ -438,8 +444,11 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(lds_cchar* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  return __builtin_bit_cast(uint16_t, (__bf16)f);
+// Two floats to a bf16 pair (lo, hi), round to nearest even: one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v_t){lo, hi}, bf16x2_t));
 }
 
 constexpr int kQKSteps = 2 * kQSteps;   // (token block, k-step) pairs of S^T = K . Q^T
@@ -549,7 +558,7 @@ __device__ __forceinline__ void softmax_tile(f32x4v_t s0, f32x4v_t s1, float& m_
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * e], scale_log2, -m_use));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * e + 1], scale_log2, -m_use));
     psum += p0 + p1;
-    pk[e] = (uint32_t)f32_to_bf16_rne(p0) | ((uint32_t)f32_to_bf16_rne(p1) << 16);
+    pk[e] = pack_bf16x2(p0, p1);
   }
   l_run += psum;
   *(__attribute__((address_space(3))) u32x4_t*)(pout + 16 * lane) = pk;
@@ -751,8 +760,8 @@ __device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
     for (int mb = 0; mb < kPVBlocks; mb++) {
       const f32x4v_t o = acc[r][mb] * inv;
       u32x2_t wv;
-      wv[0] = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
-      wv[1] = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+      wv[0] = pack_bf16x2(o[0], o[1]);
+      wv[1] = pack_bf16x2(o[2], o[3]);
       *(__attribute__((address_space(3))) u32x2_t*)(srow + 32 * mb) = wv;
     }
   }
@@ -1014,7 +1023,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(CombineArgs a) {
   u32x4_t w;
 #pragma unroll
   for (int e = 0; e < 4; e++)
-    w[e] = (uint32_t)f32_to_bf16_rne(o[2 * e] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * e + 1] * inv) << 16);
+    w[e] = pack_bf16x2(o[2 * e] * inv, o[2 * e + 1] * inv);
   *(u32x4_t*)(a.out + orow * kLatentDim + 8 * lane) = w;
   if (a.lse != nullptr && lane == 0) a.lse[orow] = den > 0.f ? M + __logf(den) : kNegInf;
 }
