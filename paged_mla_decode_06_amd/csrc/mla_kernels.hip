@@ -64,21 +64,28 @@ constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
 #endif
 constexpr int kRowsPerWave = 16 * kRowBlocksPerWave;
 static_assert(kRowBlocksPerWave == 1, "one 16-row MFMA block per wave");
-// A split workgroup runs three kinds of wave, kRowGroups of each (one of each
-// kind per SIMD), in a pipeline over the KV tiles of a piece:
-//   QK waves      S = Q.K^T for their 16 rows on tile j+1, online softmax,
-//                 P (bf16) and the rows' rescale factors out to LDS;
-//   PV waves      the same 16 rows: O = alpha*O + P.V on tile j;
-//   loader waves  tile j+3 into the LDS ring.
+// A split workgroup runs three kinds of wave in a pipeline over the KV tiles
+// of a piece (waves are spread evenly over the four SIMDs):
+//   QK waves      (kRowGroups) S = Q.K^T for their 16 rows on tile j+1,
+//                 online softmax, P (bf16) and the rows' rescale factors out
+//                 to LDS;
+//   PV waves      (kPVWaves) O = alpha*O + P.V on tile j, each for a share of
+//                 the (row group, output dims) grid;
+//   loader waves  (kLoaderWaves) tile j+3 into the LDS ring.
 // Splitting the two products over two waves gives each one registers for a
 // deep LDS read-ahead (Q and O no longer share a wave), and the softmax of
 // one wave runs while the other keeps the matrix unit busy.  A tile load can
 // stall its wave at issue for hundreds of cycles while the memory queue is
 // full; the loader waves take those stalls.
 constexpr int kRowGroups = kRowsPerBlock / kRowsPerWave;
-constexpr int kQKWave0 = 0, kPVWave0 = kRowGroups, kLoaderWave0 = 2 * kRowGroups;
+#ifndef MLA_PV_WAVES
+#define MLA_PV_WAVES 4
+#endif
+constexpr int kPVWaves = MLA_PV_WAVES;
+constexpr int kQKWave0 = 0, kPVWave0 = kRowGroups, kLoaderWave0 = kRowGroups + kPVWaves;
 constexpr int kLoaderWaves = 4;
-constexpr int kSplitWaves = 2 * kRowGroups + kLoaderWaves;
+constexpr int kSplitWaves = kRowGroups + kPVWaves + kLoaderWaves;
+static_assert(kSplitWaves % 4 == 0 && kSplitWaves <= 16, "whole waves per SIMD, at most 1024 threads");
 constexpr int kSplitThreads = 64 * kSplitWaves;
 constexpr int kLoaderThreads = 64 * kLoaderWaves;
 constexpr int kRowBytes = kRowDim * 2;             // 1152: one bf16 row in LDS
@@ -284,12 +291,22 @@ struct Stage<false> {
   // last valid token re-read the same chunk of the tile's first row, so every
   // LDS row stays finite.  A block-table entry outside [0, N) reads page 0 in
   // its place (the result is undefined then, but the count holds).  A tile
-  // with no valid token (only a request with no token at all) issues nothing.
+  // with no valid token (only a request with no token at all) issues no load
+  // and is filled with zeros.
   // Called by loader wave lw; returns the number of loads it issued (0 or kLoadsPerWave).
   __device__ __forceinline__ int issue(const SplitArgs& a, lds_char* buf, PageWindow& pw, int b, int ts,
                                        int tok_end, int lw) const {
     const int wave = lw;
-    if (ts >= tok_end) return 0;
+    if (ts >= tok_end) {
+      // no valid token (a request with no token at all): zeros instead, so
+      // that the masked scores meet finite values
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int i = 0; i < kLoadsPerWave; i++)
+        *(__attribute__((address_space(3))) u32x4_t*)(buf + wave * 1024 + kLoaderWaves * 1024 * i + 16 * lane) =
+            u32x4_t{0u, 0u, 0u, 0u};
+      return 0;
+    }
     const int32_t page = pw.page(a, b, ts / a.P);
     const int32_t pg = (uint32_t)page < (uint32_t)a.N ? page : 0;
     const char* base = (const char*)a.pool + ((int64_t)pg * a.P + (ts % a.P)) * (int64_t)kRowBytes;
@@ -430,14 +447,15 @@ __device__ __forceinline__ lds_cchar* opaque_lds(lds_cchar* p) {
 #ifndef MLA_PRIO_LD
 #define MLA_PRIO_LD 3
 #endif
-// Row groups per PV wave.  The kRowGroups PV waves split the (row group,
-// 16-dim block) grid: kPVRowGroups row groups times 1/kPVRowGroups of the 32
+// Row groups per PV wave.  The kPVWaves PV waves split the (row group,
+// 16-dim block) grid: kPVRowGroups row groups times 1/kPVDimParts of the 32
 // dim blocks each, so a V^T fragment read from LDS feeds kPVRowGroups MFMAs.
 #ifndef MLA_PV_RG
 #define MLA_PV_RG 2
 #endif
 constexpr int kPVRowGroups = MLA_PV_RG;
-constexpr int kPVDimParts = kPVRowGroups;           // dim ranges per row group
+constexpr int kPVDimParts = kPVWaves * kPVRowGroups / kRowGroups;   // dim ranges per row group
+static_assert(kPVDimParts * kRowGroups == kPVWaves * kPVRowGroups, "PV waves cover the grid exactly");
 constexpr int kPVBlocks = kVBlocks / kPVDimParts;   // 16-dim blocks of one PV wave
 static_assert(kRowGroups % kPVRowGroups == 0 && kPVBlocks % 4 == 0, "PV work split");
 __device__ __forceinline__ s16x4_t lds_read_tr16(lds_cchar* p) {
@@ -766,12 +784,13 @@ __device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
     }
   }
   lds_barrier();   // every row is staged
-  // Wave v copies out rows 16v .. 16v+15 and their LSEs: lane l carries bytes
-  // 16l .. 16l+15 of a row.
+  // Wave v copies out rows kCopyRows*v .. +kCopyRows and their LSEs: lane l
+  // carries bytes 16l .. 16l+15 of a row.
+  constexpr int kCopyRows = kRowsPerBlock / kPVWaves;
   {
-    const int rib = 16 * v + i16;
+    const int rib = kCopyRows * v + i16;
     const int row = pc.rb * kRowsPerBlock + rib;
-    if (row < a.R && g == 0) {
+    if (row < a.R && g == 0 && i16 < kCopyRows) {
       const float m_run = stats[2 * rib], l_tot = stats[2 * rib + 1];
       const float lse_nat = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
       if (pc.slot < 0) {
@@ -784,8 +803,8 @@ __device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
       }
     }
   }
-  for (int rr = 0; rr < 16; rr++) {
-    const int r_in = 16 * v + rr;
+  for (int rr = 0; rr < kCopyRows; rr++) {
+    const int r_in = kCopyRows * v + rr;
     const int r = pc.rb * kRowsPerBlock + r_in;
     if (r >= a.R) break;
     const u32x4_t o = *(__attribute__((address_space(3))) const u32x4_t*)(lds + r_in * kStagePitch + 16 * lane);
@@ -829,6 +848,61 @@ __device__ void build_unit_offsets(const int32_t* seq_lens, int32_t B, int32_t m
   __syncthreads();
 }
 
+// Balanced mode with B <= 64 * kWaveScanPer: the same offsets computed by one
+// wave alone, with no LDS and no barrier: lane l sums the units of requests
+// l*per .. l*per+per-1, a prefix over the lanes places them, and the lane
+// whose range holds unit u_begin names the first request of the workgroup.
+// With publish, the wave also writes unit_off[0..B] for the combine.
+constexpr int kWaveScanPer = 16;
+struct ShareStart {
+  int32_t total, b_first, off_first;
+};
+__device__ ShareStart wave_share_start(const SplitArgs& a, int64_t grp, bool publish) {
+  const int lane = threadIdx.x & 63;
+  const int per = (a.B + 63) / 64;
+  const int b0 = lane * per;
+  int32_t u[kWaveScanPer];
+  int32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < kWaveScanPer; i++) {
+    const int b = b0 + i;
+    u[i] = i < per && b < a.B ? units_of(clamp_len(a.seq_lens[b], a.max_seq_len)) : 0;
+    sum += u[i];
+  }
+  int32_t incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t t = __shfl_up(incl, d);
+    if (lane >= d) incl += t;
+  }
+  ShareStart r;
+  r.total = __builtin_amdgcn_readlane(incl, 63);
+  const int64_t u_begin = wg_start(grp, r.total, a.NG);
+  int32_t run = incl - sum, found_b = -1, found_off = 0;
+#pragma unroll
+  for (int i = 0; i < kWaveScanPer; i++) {
+    const int b = b0 + i;
+    if (i < per && b < a.B) {
+      if (publish) a.unit_off_ws[b] = run;
+      if (run <= u_begin && u_begin < run + u[i]) {
+        found_b = b;
+        found_off = run;
+      }
+    }
+    run += u[i];
+  }
+  if (publish && lane == 63) a.unit_off_ws[a.B] = r.total;
+  const uint64_t hit = __ballot(found_b >= 0);
+  r.b_first = 0;
+  r.off_first = 0;
+  if (hit != 0) {
+    const int src = __builtin_ctzll(hit);
+    r.b_first = __builtin_amdgcn_readlane(found_b, src);
+    r.off_first = __builtin_amdgcn_readlane(found_off, src);
+  }
+  return r;
+}
+
 __device__ __forceinline__ int32_t find_request(const int32_t* off, int32_t B, int64_t u) {
   int lo = 0, hi = B - 1;   // largest b with off[b] <= u
   while (lo < hi) {
@@ -861,27 +935,34 @@ __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a
   int64_t grp;
   int32_t rb;
   group_of_block(blockIdx.x, a.nrb, &grp, &rb);
-  // Balanced mode: the unit offsets of all requests are built in the tile
-  // buffers' LDS (before any tile is loaded), block 0 publishes them for the
-  // combine, and this workgroup keeps only where its share starts.
+  // Balanced mode: the unit offsets of all requests, of which this workgroup
+  // keeps only where its share starts; block 0 publishes them for the
+  // combine.  Up to 64 * kWaveScanPer requests every wave computes them on its
+  // own; larger batches build them block-wide in the tile buffers' LDS
+  // (before any tile is loaded).  Every LDS byte a wave reads later is written
+  // first in the pipeline (tiles by loads or zero fills), so nothing is
+  // cleared here.
   int32_t total = 0, b_first = 0, off_first = 0;
   if (a.num_splits == 0) {
-    int32_t* off = (int32_t*)smem;
-    build_unit_offsets<kSplitThreads>(a.seq_lens, a.B, a.max_seq_len, off, off + kMaxBatch + 1);
-    if (blockIdx.x == 0)
-      for (int b = threadIdx.x; b <= a.B; b += kSplitThreads) a.unit_off_ws[b] = off[b];
-    total = __builtin_amdgcn_readfirstlane(off[a.B]);
-    const int64_t u_begin = wg_start(grp, total, a.NG);
-    if (u_begin < total) {
-      b_first = __builtin_amdgcn_readfirstlane(find_request(off, a.B, u_begin));
-      off_first = __builtin_amdgcn_readfirstlane(off[b_first]);
+    if (a.B <= 64 * kWaveScanPer) {
+      const ShareStart st = wave_share_start(a, grp, blockIdx.x == 0 && threadIdx.x < 64);
+      total = __builtin_amdgcn_readfirstlane(st.total);
+      b_first = __builtin_amdgcn_readfirstlane(st.b_first);
+      off_first = __builtin_amdgcn_readfirstlane(st.off_first);
+    } else {
+      int32_t* off = (int32_t*)smem;
+      build_unit_offsets<kSplitThreads>(a.seq_lens, a.B, a.max_seq_len, off, off + kMaxBatch + 1);
+      if (blockIdx.x == 0)
+        for (int b = threadIdx.x; b <= a.B; b += kSplitThreads) a.unit_off_ws[b] = off[b];
+      total = __builtin_amdgcn_readfirstlane(off[a.B]);
+      const int64_t u_begin = wg_start(grp, total, a.NG);
+      if (u_begin < total) {
+        b_first = __builtin_amdgcn_readfirstlane(find_request(off, a.B, u_begin));
+        off_first = __builtin_amdgcn_readfirstlane(off[b_first]);
+      }
+      __syncthreads();   // every wave has read the offsets before tiles land there
     }
-    __syncthreads();   // every wave has read the offsets before the buffers are cleared
   }
-  // Tiles a load skips keep what is in LDS; start from zeros.
-  for (int i = threadIdx.x; i < kTileBufs * kTileBytes / 16; i += kSplitThreads)
-    ((__attribute__((address_space(3))) u32x4_t*)tiles)[i] = u32x4_t{0u, 0u, 0u, 0u};
-  lds_barrier();
   if (grp >= a.NG) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave >= kLoaderWave0) {

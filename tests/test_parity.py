@@ -113,3 +113,16 @@ def test_full_size_repeatable(name):
                     rows = (outs[k].view(torch.int16) != ref_o.view(torch.int16)).any(dim=-1).nonzero()
                     differing.append((it - 7 + k, rows[:4].tolist()))
     assert not differing, f"{name}: {len(differing)} of 160 calls differ from the first, e.g. {differing[:3]}"
+
+
+@pytest.mark.parametrize("B", [700, 1500])
+def test_many_requests(orc, B):
+    """Large batches of short requests, some empty: the workgroup plan is found
+    by one wave per workgroup up to 1024 requests and block-wide beyond."""
+    rng = np.random.default_rng(50 + B)
+    lens = rng.integers(0, 70, size=B)
+    lens[::97] = 0
+    inp = P.small(lens=tuple(int(x) for x in lens), heads=16, seed=51)
+    ro, rl = orc.decode(inp)
+    o, l = G.run(inp)
+    G.compare(o, l, ro, rl, what=f"B={B}")
