@@ -32,6 +32,7 @@ LATENT_DIM = 512
 ROPE_DIM = 64
 ROWS_PER_BLOCK = 64     # query rows per workgroup
 TILE = 32               # tokens per KV tile
+PIECE_COST = 8          # balanced plan: start-up cost of a piece, in tiles
 
 
 class MlaError(RuntimeError):

@@ -73,9 +73,9 @@ mla_status check_params(const mla_decode_params* p) {
   if (p->kv_dtype == MLA_KV_FP8_E4M3FN && !finite_pos(p->k_scale)) return MLA_ERR_INVALID_VALUE;
   if (p->num_splits < 0 || p->num_splits > kMaxSplits) return MLA_ERR_INVALID_VALUE;
   if (p->min_work_units < 0 || p->num_cus < 0) return MLA_ERR_INVALID_VALUE;
-  // Work units are counted in int32 on the device.
+  // Work units and the balanced plan's cost positions are counted in int32 on the device.
   const int64_t nrb = mla::row_blocks(p->q_len, p->num_heads);
-  if ((int64_t)p->batch * nrb * mla::units_of(p->max_seq_len) >= ((int64_t)1 << 31)) return MLA_ERR_NOT_SUPPORTED;
+  if ((int64_t)p->batch * nrb * mla::positions_of(p->max_seq_len) >= ((int64_t)1 << 31)) return MLA_ERR_NOT_SUPPORTED;
   return MLA_OK;
 }
 
@@ -96,7 +96,7 @@ mla_status target_units(const mla_decode_params* p, int32_t* target) {
 
 struct Layout {
   int64_t groups = 0, wgs = 0, slots = 0;
-  size_t off_unit = 0, off_lse = 0, off_o = 0, total = 0;
+  size_t off_pos = 0, off_lse = 0, off_o = 0, total = 0;
 };
 
 mla_status layout_of(const mla_decode_params* p, Layout* lay) {
@@ -109,7 +109,7 @@ mla_status layout_of(const mla_decode_params* p, Layout* lay) {
   lay->groups = mla::group_count(p->batch, nrb, p->max_seq_len, p->num_splits, target);
   lay->wgs = lay->groups * nrb;
   lay->slots = mla::slot_count(lay->groups, nrb, p->num_splits);
-  lay->off_unit = 0;
+  lay->off_pos = 0;
   lay->off_lse = align256(((size_t)p->batch + 1) * sizeof(int32_t));
   lay->off_o = lay->off_lse + align256((size_t)lay->slots * kRowsPerBlock * sizeof(float));
   lay->total = lay->off_o + (size_t)lay->slots * kRowsPerBlock * kLatentDim * sizeof(uint16_t);
@@ -178,7 +178,7 @@ static mla_status decode_impl(const mla_decode_params* p, const void* q, const v
   a.lse = lse;
   a.part_o = (uint16_t*)(ws + lay.off_o);
   a.part_lse = (float*)(ws + lay.off_lse);
-  a.unit_off_ws = (int32_t*)(ws + lay.off_unit);
+  a.pos_off_ws = (int32_t*)(ws + lay.off_pos);
   a.B = p->batch;
   a.q_len = p->q_len;
   a.H = p->num_heads;
@@ -200,7 +200,7 @@ static mla_status decode_impl(const mla_decode_params* p, const void* q, const v
     mla::CombineArgs c;
     c.part_o = a.part_o;
     c.part_lse = a.part_lse;
-    c.unit_off_ws = a.unit_off_ws;
+    c.pos_off_ws = a.pos_off_ws;
     c.seq_lens = seq_lens;
     c.out = a.out;
     c.lse = lse;
@@ -283,7 +283,7 @@ mla_status mla_plan_host(const mla_decode_params* p, const int32_t* seq_lens_hos
   } else {
     std::vector<int64_t> off((size_t)B + 1, 0);
     for (int32_t b = 0; b < B; b++)
-      off[b + 1] = off[b] + mla::units_of(mla::clamp_len(seq_lens_host[b], p->max_seq_len));
+      off[b + 1] = off[b] + mla::positions_of(mla::clamp_len(seq_lens_host[b], p->max_seq_len));
     auto fr = [&](int64_t u) -> int32_t {   // largest b with off[b] <= u
       int32_t lo = 0, hi = B - 1;
       while (lo < hi) {
@@ -295,8 +295,8 @@ mla_status mla_plan_host(const mla_decode_params* p, const int32_t* seq_lens_hos
     auto units = [&](int32_t b) -> int32_t { return mla::units_of(mla::clamp_len(seq_lens_host[b], p->max_seq_len)); };
     const int64_t total = off[(size_t)B];
     for (int64_t g = 0; g < NG; g++) {
-      const int64_t u_begin = mla::wg_start(g, total, NG);
-      const int32_t b_first = u_begin < total ? fr(u_begin) : 0;
+      const int64_t v_begin = mla::wg_start(g, total, NG);
+      const int32_t b_first = v_begin < total ? fr(v_begin) : 0;
       for (int32_t rb = 0; rb < nrb; rb++)
         mla::balanced_pieces(g, NG, rb, nrb, total, b_first, off[(size_t)b_first], units,
                              [&](const mla::Piece& pc) { emit(pc, g * nrb + rb); });

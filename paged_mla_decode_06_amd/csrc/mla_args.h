@@ -14,7 +14,7 @@ struct SplitArgs {
   float* lse;               // [B][q_len][H] or null
   uint16_t* part_o;         // [slots][64][512] bf16, normalised partial outputs
   float* part_lse;          // [slots][64]
-  int32_t* unit_off_ws;     // [B+1] (balanced mode), written by workgroup 0
+  int32_t* pos_off_ws;      // [B+1] cost-position offsets (balanced mode), written by workgroup 0
   int32_t B, q_len, H, P, W, N, max_seq_len, nrb, R, num_splits;
   int64_t NG;   // groups of the plan
   float scale_log2;         // softmax_scale * (k_scale for fp8) * log2(e)
@@ -24,7 +24,7 @@ struct SplitArgs {
 struct CombineArgs {
   const uint16_t* part_o;
   const float* part_lse;
-  const int32_t* unit_off_ws;
+  const int32_t* pos_off_ws;
   const int32_t* seq_lens;
   uint16_t* out;
   float* lse;

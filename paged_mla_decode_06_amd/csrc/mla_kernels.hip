@@ -820,16 +820,17 @@ __device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
   lds_barrier();   // every wave has read its rows before the next piece's tile loads land there
 }
 
-// Block-wide computation of unit_off[0..B] into LDS (balanced mode).
+// Block-wide computation of the balanced plan's cost-position offsets
+// off[0..B] into LDS.
 // part: NT ints of LDS scratch.
 template <int NT>
-__device__ void build_unit_offsets(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t* off,
+__device__ void build_pos_offsets(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t* off,
                                    int32_t* part) {
   const int tid = threadIdx.x;
   const int per = (B + NT - 1) / NT;
   const int b0 = tid * per, b1 = min(B, b0 + per);
   int32_t sum = 0;
-  for (int b = b0; b < b1; b++) sum += units_of(clamp_len(seq_lens[b], max_seq_len));
+  for (int b = b0; b < b1; b++) sum += positions_of(clamp_len(seq_lens[b], max_seq_len));
   part[tid] = sum;
   __syncthreads();
   // inclusive scan of part[] (Hillis-Steele)
@@ -842,17 +843,17 @@ __device__ void build_unit_offsets(const int32_t* seq_lens, int32_t B, int32_t m
   int32_t run = tid == 0 ? 0 : part[tid - 1];
   for (int b = b0; b < b1; b++) {
     off[b] = run;
-    run += units_of(clamp_len(seq_lens[b], max_seq_len));
+    run += positions_of(clamp_len(seq_lens[b], max_seq_len));
   }
   if (tid == NT - 1) off[B] = part[NT - 1];
   __syncthreads();
 }
 
 // Balanced mode with B <= 64 * kWaveScanPer: the same offsets computed by one
-// wave alone, with no LDS and no barrier: lane l sums the units of requests
-// l*per .. l*per+per-1, a prefix over the lanes places them, and the lane
-// whose range holds unit u_begin names the first request of the workgroup.
-// With publish, the wave also writes unit_off[0..B] for the combine.
+// wave alone, with no LDS and no barrier: lane l sums the cost positions of
+// requests l*per .. l*per+per-1, a prefix over the lanes places them, and the
+// lane whose range holds position start(g) names the first request of the
+// workgroup.  With publish, the wave also writes off[0..B] for the combine.
 constexpr int kWaveScanPer = 16;
 struct ShareStart {
   int32_t total, b_first, off_first;
@@ -866,7 +867,7 @@ __device__ ShareStart wave_share_start(const SplitArgs& a, int64_t grp, bool pub
 #pragma unroll
   for (int i = 0; i < kWaveScanPer; i++) {
     const int b = b0 + i;
-    u[i] = i < per && b < a.B ? units_of(clamp_len(a.seq_lens[b], a.max_seq_len)) : 0;
+    u[i] = i < per && b < a.B ? positions_of(clamp_len(a.seq_lens[b], a.max_seq_len)) : 0;
     sum += u[i];
   }
   int32_t incl = sum;
@@ -877,21 +878,21 @@ __device__ ShareStart wave_share_start(const SplitArgs& a, int64_t grp, bool pub
   }
   ShareStart r;
   r.total = __builtin_amdgcn_readlane(incl, 63);
-  const int64_t u_begin = wg_start(grp, r.total, a.NG);
+  const int64_t v_begin = wg_start(grp, r.total, a.NG);
   int32_t run = incl - sum, found_b = -1, found_off = 0;
 #pragma unroll
   for (int i = 0; i < kWaveScanPer; i++) {
     const int b = b0 + i;
     if (i < per && b < a.B) {
-      if (publish) a.unit_off_ws[b] = run;
-      if (run <= u_begin && u_begin < run + u[i]) {
+      if (publish) a.pos_off_ws[b] = run;
+      if (run <= v_begin && v_begin < run + u[i]) {
         found_b = b;
         found_off = run;
       }
     }
     run += u[i];
   }
-  if (publish && lane == 63) a.unit_off_ws[a.B] = r.total;
+  if (publish && lane == 63) a.pos_off_ws[a.B] = r.total;
   const uint64_t hit = __ballot(found_b >= 0);
   r.b_first = 0;
   r.off_first = 0;
@@ -935,7 +936,7 @@ __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a
   int64_t grp;
   int32_t rb;
   group_of_block(blockIdx.x, a.nrb, &grp, &rb);
-  // Balanced mode: the unit offsets of all requests, of which this workgroup
+  // Balanced mode: the cost-position offsets of all requests, of which this workgroup
   // keeps only where its share starts; block 0 publishes them for the
   // combine.  Up to 64 * kWaveScanPer requests every wave computes them on its
   // own; larger batches build them block-wide in the tile buffers' LDS
@@ -951,13 +952,13 @@ __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a
       off_first = __builtin_amdgcn_readfirstlane(st.off_first);
     } else {
       int32_t* off = (int32_t*)smem;
-      build_unit_offsets<kSplitThreads>(a.seq_lens, a.B, a.max_seq_len, off, off + kMaxBatch + 1);
+      build_pos_offsets<kSplitThreads>(a.seq_lens, a.B, a.max_seq_len, off, off + kMaxBatch + 1);
       if (blockIdx.x == 0)
-        for (int b = threadIdx.x; b <= a.B; b += kSplitThreads) a.unit_off_ws[b] = off[b];
+        for (int b = threadIdx.x; b <= a.B; b += kSplitThreads) a.pos_off_ws[b] = off[b];
       total = __builtin_amdgcn_readfirstlane(off[a.B]);
-      const int64_t u_begin = wg_start(grp, total, a.NG);
-      if (u_begin < total) {
-        b_first = __builtin_amdgcn_readfirstlane(find_request(off, a.B, u_begin));
+      const int64_t v_begin = wg_start(grp, total, a.NG);
+      if (v_begin < total) {
+        b_first = __builtin_amdgcn_readfirstlane(find_request(off, a.B, v_begin));
         off_first = __builtin_amdgcn_readfirstlane(off[b_first]);
       }
       __syncthreads();   // every wave has read the offsets before tiles land there
@@ -991,7 +992,9 @@ __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a
 // 512-wide bf16 partials are summed with weights exp(lse_s - LSE).
 constexpr int kCombineRowsPerBlock = kThreads / 64;
 
-__global__ __launch_bounds__(kThreads) void mla_combine_kernel(CombineArgs a) {
+// At most 64 VGPRs: eight workgroups per CU, so the grid of a full-size decode
+// (up to 2048 workgroups) runs in one round.
+__global__ __launch_bounds__(kThreads, 8) void mla_combine_kernel(CombineArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int chunks = kRowsPerBlock / kCombineRowsPerBlock;
   const int64_t blk = blockIdx.x / chunks;     // b * nrb + rb
@@ -1001,23 +1004,23 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(CombineArgs a) {
   if (row >= a.R) return;
   const int32_t U = units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
   // the pieces of this row block: groups [g0, g1]
-  int64_t g0, g1, first_unit = 0, total = 0;
+  int64_t g0, g1, first_pos = 0, total = 0;
   if (a.num_splits > 0) {
     const int32_t Sp = a.num_splits < U ? a.num_splits : U;
     if (Sp <= 1) return;
     g0 = (int64_t)b * a.num_splits;
     g1 = g0 + Sp - 1;
   } else {
-    total = a.unit_off_ws[a.B];
-    first_unit = a.unit_off_ws[b];
-    g0 = wg_of_unit(first_unit, total, a.NG);
-    g1 = wg_of_unit(first_unit + U - 1, total, a.NG);
+    total = a.pos_off_ws[a.B];
+    first_pos = a.pos_off_ws[b];
+    g0 = first_group(first_pos, total, a.NG);
+    g1 = last_group(first_pos, U, total, a.NG);
     if (g0 == g1) return;
   }
   auto slot_of = [&](int64_t g) -> int64_t {
     if (a.num_splits > 0) return g * a.nrb + rb;
     if (wg_start(g, total, a.NG) == wg_start(g + 1, total, a.NG)) return -1;   // an empty group
-    return balanced_slot(g, g0, first_unit, total, a.NG, rb, a.nrb);
+    return balanced_slot(g, g0, first_pos, total, a.NG, rb, a.nrb);
   };
   const int64_t n = g1 - g0 + 1;
   // Lane l handles piece c0 + l of each chunk of 64: its slot, its LSE and
@@ -1147,7 +1150,7 @@ __global__ __launch_bounds__(kThreads) void mla_plan_kernel(const int32_t* seq_l
     n++;
   };
   __shared__ int32_t part[kThreads];
-  if (num_splits == 0) build_unit_offsets<kThreads>(seq_lens, B, max_seq_len, off, part);
+  if (num_splits == 0) build_pos_offsets<kThreads>(seq_lens, B, max_seq_len, off, part);
   if (grp >= NG) return;
   if (num_splits > 0) {
     const int32_t b = (int32_t)(grp / num_splits);
@@ -1155,8 +1158,8 @@ __global__ __launch_bounds__(kThreads) void mla_plan_kernel(const int32_t* seq_l
     if (forced_piece(grp, rb, nrb, num_splits, units_of(clamp_len(seq_lens[b], max_seq_len)), &pc)) emit(pc);
   } else {
     const int32_t total = off[B];
-    const int64_t u_begin = wg_start(grp, total, NG);
-    const int32_t b_first = u_begin < total ? find_request(off, B, u_begin) : 0;
+    const int64_t v_begin = wg_start(grp, total, NG);
+    const int32_t b_first = v_begin < total ? find_request(off, B, v_begin) : 0;
     auto units = [&](int32_t b) -> int32_t { return units_of(clamp_len(seq_lens[b], max_seq_len)); };
     balanced_pieces(grp, NG, rb, nrb, total, b_first, off[b_first], units, emit);
   }

@@ -14,12 +14,17 @@
 //
 // Balanced mode (num_splits == 0), in the spirit of the tile-scheduler
 // metadata the pages obtain from get_mla_metadata ("tokenspeed flashmla.py",
-// FlashMLABackend._init_decode_metadata): NG groups each take a contiguous,
-// equal share [start(g), start(g+1)) of all units, start(g) =
-// floor(g*total/NG), cut into pieces at request boundaries.  A piece that
-// covers a whole request writes the output; any other piece writes a partial
-// result to slot 2*wg (the group's first piece) or 2*wg+1 (its last piece),
-// wg = g*nrb + rb, and the combine merges the partials of a row block.
+// FlashMLABackend._init_decode_metadata), with a fixed start-up cost per
+// piece.  The requests are laid out on a line of cost positions: request b
+// takes kPieceCost + U_b of them, its start-up cost first (the latency of
+// its first tiles, the query load, the epilogue), then one per tile.  NG
+// groups each take a contiguous, equal share [start(g), start(g+1)) of all
+// positions, start(g) = floor(g*total/NG); the tiles of each request that
+// fall in a share form that group's piece of the request, so a group that
+// starts more pieces gets fewer tiles.  A piece that covers a whole request
+// writes the output; any other piece writes a partial result to slot 2*wg
+// (the group's first piece) or 2*wg+1 (its last piece), wg = g*nrb + rb, and
+// the combine merges the partials of a row block.
 //
 // Forced mode (num_splits = S > 0): group g = b*S + s takes piece s of the
 // S' = min(S, U) near-equal pieces of request b; slot wg when S' > 1.
@@ -48,13 +53,20 @@ MLA_HD int32_t units_of(int32_t L) {
   int32_t u = (L + kTile - 1) / kTile;
   return u < 1 ? 1 : u;
 }
+// Balanced-mode start-up cost of a piece, in tiles of the steady stream.
+#ifndef MLA_PIECE_COST
+#define MLA_PIECE_COST 8
+#endif
+constexpr int kPieceCost = MLA_PIECE_COST;
+// Cost positions request b takes in balanced mode.
+MLA_HD int32_t positions_of(int32_t L) { return kPieceCost + units_of(L); }
 MLA_HD int32_t row_blocks(int32_t q_len, int32_t heads) {
   return (q_len * heads + kRowsPerBlock - 1) / kRowsPerBlock;
 }
-// First unit of group g in balanced mode.
+// First cost position of group g in balanced mode (total positions in all).
 MLA_HD int64_t wg_start(int64_t g, int64_t total, int64_t G) { return g * total / G; }
-// The group whose share holds unit u (0 <= u < total): the largest g with start(g) <= u.
-MLA_HD int64_t wg_of_unit(int64_t u, int64_t total, int64_t G) { return ((u + 1) * G - 1) / total; }
+// The group whose share holds position v (0 <= v < total): the largest g with start(g) <= v.
+MLA_HD int64_t wg_of_pos(int64_t v, int64_t total, int64_t G) { return ((v + 1) * G - 1) / total; }
 
 // Groups of the plan.  Balanced: about target workgroups, never more groups
 // than B * units_of(max_seq_len) (which bounds the true unit count).
@@ -85,38 +97,46 @@ struct Piece {
 };
 
 // Pieces of balanced-mode group g for row block rb, one at a time.  total is
-// the number of units of all requests; b_first is the request holding the
-// group's first unit start(g) (off(b_first) <= start(g) < off(b_first + 1),
-// off(b) = sum of U_b' for b' < b) and off_first = off(b_first).  The
-// requests of the share are walked in order, so no table of offsets is
-// needed; next(units, &pc) yields the following piece (units(b) returns U_b)
-// or false after the last.
+// the number of cost positions of all requests; b_first is the request
+// holding the group's first position start(g) (off(b_first) <= start(g) <
+// off(b_first + 1), off(b) = sum of positions_of(L_b') for b' < b) and
+// off_first = off(b_first).  The requests of the share are walked in order,
+// so no table of offsets is needed; next(units, &pc) yields the following
+// piece (units(b) returns U_b) or false after the last.  A share that ends
+// inside a request's start-up positions holds none of its tiles.
 struct BalancedWalk {
-  int64_t u, u_begin, u_end, ob, wg;
+  int64_t v, v_end, ob, wg;
   int32_t b, rb;
+  bool first;
   MLA_HD void init(int64_t g, int64_t G, int32_t rb_, int32_t nrb, int64_t total, int32_t b_first,
                    int64_t off_first) {
-    u_begin = wg_start(g, total, G);
-    u_end = wg_start(g + 1, total, G);
-    u = u_begin;
+    v = wg_start(g, total, G);
+    v_end = wg_start(g + 1, total, G);
     ob = off_first;
     wg = g * nrb + rb_;
     b = b_first;
     rb = rb_;
+    first = true;
   }
   template <class Units>
   MLA_HD bool next(const Units& units, Piece* pc) {
-    if (u >= u_end) return false;
+    if (v >= v_end) return false;
     const int32_t U = units(b);
-    const int64_t oe = ob + U;
-    const int64_t pe = oe < u_end ? oe : u_end;
+    const int64_t oe = ob + kPieceCost + U;      // end of request b's positions
+    const int64_t pe = oe < v_end ? oe : v_end;  // end of this piece's positions
+    const int64_t t0 = v - ob - kPieceCost, t1 = pe - ob - kPieceCost;
+    if (t1 <= 0) {   // only start-up positions: the share ends here
+      v = v_end;
+      return false;
+    }
     pc->b = b;
     pc->rb = rb;
-    pc->tile0 = (int32_t)(u - ob);
-    pc->tile1 = (int32_t)(pe - ob);
+    pc->tile0 = t0 > 0 ? (int32_t)t0 : 0;
+    pc->tile1 = (int32_t)t1;
     const bool whole = pc->tile0 == 0 && pc->tile1 == U;
-    pc->slot = whole ? -1 : (int32_t)(2 * wg + (u == u_begin ? 0 : 1));
-    u = pe;
+    pc->slot = whole ? -1 : (int32_t)(2 * wg + (first ? 0 : 1));
+    first = false;
+    v = pe;
     ob = oe;
     b++;
     return true;
@@ -149,11 +169,20 @@ MLA_HD bool forced_piece(int64_t g, int32_t rb, int32_t nrb, int32_t S, int32_t 
   return true;
 }
 
-// Slot of the piece that group g contributes to row block rb of a request
-// whose units start at first_unit (balanced mode, g in [g0, g1]).
-MLA_HD int64_t balanced_slot(int64_t g, int64_t g0, int64_t first_unit, int64_t total, int64_t G, int32_t rb,
+// The groups holding pieces of a request whose positions start at first_pos
+// and that has U tiles (balanced mode): g0 holds its first tile, g1 its last.
+MLA_HD int64_t first_group(int64_t first_pos, int64_t total, int64_t G) {
+  return wg_of_pos(first_pos + kPieceCost, total, G);
+}
+MLA_HD int64_t last_group(int64_t first_pos, int32_t U, int64_t total, int64_t G) {
+  return wg_of_pos(first_pos + kPieceCost + U - 1, total, G);
+}
+// Slot of the piece that group g contributes to row block rb of that request
+// (g in [g0, g1], group g's share not empty).  Group g0 holds a piece of an
+// earlier request first exactly when its share starts before first_pos.
+MLA_HD int64_t balanced_slot(int64_t g, int64_t g0, int64_t first_pos, int64_t total, int64_t G, int32_t rb,
                              int32_t nrb) {
-  const bool second = g == g0 && wg_start(g0, total, G) != first_unit;
+  const bool second = g == g0 && wg_start(g0, total, G) < first_pos;
   return 2 * (g * nrb + rb) + (second ? 1 : 0);
 }
 

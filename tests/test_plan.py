@@ -1,6 +1,6 @@
 """The split-KV work plan on the host (no GPU): every (request, row block)
 is covered exactly once, partial slots are unique, the balanced grid is
-evenly loaded."""
+evenly loaded once each piece's start-up cost is counted."""
 import math
 
 import numpy as np
@@ -38,6 +38,33 @@ def check_cover(p, L, pieces, grid):
     return cover
 
 
+def model_balanced_plan(L, max_len, nrb, NG, c):
+    """The balanced plan written out from its definition: request b takes c
+    start-up positions and then one position per 32-token tile; group g takes
+    positions [g*T//NG, (g+1)*T//NG); the tiles of a request inside a group's
+    positions form its piece; a partial piece goes to slot 2*wg if it is the
+    group's first piece, else 2*wg+1."""
+    U = [max(1, -(-min(max(int(x), 0), max_len) // mla.TILE)) for x in L]
+    off = [0]
+    for u in U:
+        off.append(off[-1] + c + u)
+    T = off[-1]
+    out = []
+    for g in range(NG):
+        v0, v1 = g * T // NG, (g + 1) * T // NG
+        for rb in range(nrb):
+            wg = g * nrb + rb
+            first = True
+            for b in range(len(U)):
+                s = off[b] + c          # position of tile 0
+                t0, t1 = max(v0, s) - s, min(v1, off[b + 1]) - s
+                if t1 > t0:
+                    whole = t0 == 0 and t1 == U[b]
+                    out.append((wg, b, rb, t0, t1, -1 if whole else 2 * wg + (0 if first else 1)))
+                    first = False
+    return sorted(out)
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_balanced_plan_covers_and_balances(seed):
     rng = np.random.default_rng(seed)
@@ -50,11 +77,18 @@ def test_balanced_plan_covers_and_balances(seed):
     p = params(B, q_len, H, int(max(L.max(), 1)), num_cus=int(rng.choice([8, 256, 512])))
     pieces, grid = mla.mla_plan_host(p, L)
     check_cover(p, L, pieces, grid)
-    # each workgroup's units differ by at most one
-    units = np.zeros(grid, dtype=np.int64)
+    nrb = -(-q_len * H // mla.ROWS_PER_BLOCK)
+    assert sorted(map(tuple, np.asarray(pieces).tolist())) == \
+        model_balanced_plan(L, p.max_seq_len, nrb, grid // nrb, mla.PIECE_COST)
+    # each workgroup's cost, its tiles plus the start-up cost of every request
+    # whose first tile it holds, is within the start-up cost of an equal share
+    c = mla.PIECE_COST
+    cost = np.zeros(grid, dtype=np.int64)
     for g, b, rb, t0, t1, slot in pieces:
-        units[g] += t1 - t0
-    assert units.max() - units.min() <= 1
+        cost[g] += (t1 - t0) + (c if t0 == 0 else 0)
+    U = np.maximum(1, -(-np.clip(L, 0, p.max_seq_len) // mla.TILE)).astype(np.int64)
+    share = (U.sum() + c * B) / (grid // nrb)
+    assert np.all(np.abs(cost - share) <= c + 1)
     # at most two partial pieces per workgroup
     part = np.zeros(grid, dtype=np.int64)
     for g, b, rb, t0, t1, slot in pieces:
