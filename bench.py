@@ -53,6 +53,10 @@ class HipEvents:
             raise RuntimeError("hipEventCreate failed")
         return ev.value
 
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(int(stream.cuda_stream))) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
         if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
@@ -89,6 +93,33 @@ def cpu_baseline(inp, budget_s: float = 10.0):
             "sample": f"{done} whole requests in batch order{passes} (all {inp.q_len * inp.heads} query rows "
                       f"each, {int(lens.sum())} cached tokens), fp64 C oracle, OpenMP over query rows; "
                       f"rate = the sample's algorithmic bytes / its time"}
+
+
+def time_kv_append(ev, stream, pool, rows, locs, k_scale: float, kv_bytes: int, reps: int = 200):
+    """Mean duration of one mla_kv_append launch (HIP events around `reps`
+    back-to-back launches on `stream`, after 20 untimed ones) writing rows
+    [T, 576] bf16 at flat slots locs into pool, and its HBM roofline."""
+    import torch
+    import paged_mla_decode_06_amd as mla
+    nope, rope = rows[:, :512], rows[:, 512:]
+    p = mla.make_append_params(rows.shape[0], pool.shape[1], pool.shape[0],
+                               mla.MLA_KV_FP8_E4M3FN if kv_bytes == 1 else mla.MLA_KV_BF16, k_scale,
+                               rows.stride(0), rows.stride(0))
+    for _ in range(20):
+        mla.mla_kv_append(nope, rope, locs, pool, stream=stream, params=p)
+    a, b = ev.create(), ev.create()
+    ev.record(a, stream)
+    for _ in range(reps):
+        mla.mla_kv_append(nope, rope, locs, pool, stream=stream, params=p)
+    ev.record(b, stream)
+    torch.cuda.synchronize()
+    us = ev.elapsed_ms(a, b) * 1e3 / reps
+    ev.destroy(a)
+    ev.destroy(b)
+    nbytes = mla.append_work(rows.shape[0], kv_bytes)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"rows": int(rows.shape[0]), "us": round(us, 3), "bytes": nbytes, "achieved": round(gbs, 2),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "mla_append_kernel"}
 
 
 def kernel_sources_sha256() -> str:
@@ -217,6 +248,23 @@ def main():
             ev.destroy(x)
     assert torch.isfinite(out.float()).all().item(), "non-finite output"
 
+    # The KV-cache append that precedes each decode step, timed on its own
+    # after the decode: the B*q_len new rows into their slots (the newest
+    # tokens of each request), and a prefill-sized append of 32768 rows at
+    # scattered slots.  Both write into a rotating pool copy the decode no
+    # longer uses.
+    P = inp.page_size
+    new_locs = [int(inp.block_table[b, t // P]) * P + t % P
+                for b in range(inp.batch) for t in range(max(int(inp.seq_lens[b]) - inp.q_len, 0),
+                                                        int(inp.seq_lens[b]))]
+    step_rows = q0.view(-1, 576)[:len(new_locs)]
+    step_locs = torch.tensor(new_locs, dtype=torch.int64, device=dev)
+    n_big = min(32768, inp.num_pages * P)
+    big_locs = torch.from_numpy(np.random.default_rng(99).permutation(inp.num_pages * P)[:n_big].astype(np.int64)).to(dev)
+    big_rows = torch.empty((n_big, 576), dtype=torch.bfloat16, device=dev).normal_()
+    append_step = time_kv_append(ev, stream, pools[-1], step_rows, step_locs, inp.k_scale, kv_bytes)
+    append_big = time_kv_append(ev, stream, pools[-1], big_rows, big_locs, inp.k_scale, kv_bytes)
+
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     kv_only = int(inp.seq_lens.astype(np.int64).sum()) * 576 * kv_bytes
     # the split kernel's own algorithmic bytes: everything but the output rows
@@ -252,6 +300,8 @@ def main():
                      "kernel": "mla_split_kernel", "algorithmic_bytes_per_launch": split_bytes,
                      "mfma_frac": round(flops / (split_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
         "path_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+        "kv_append": append_step,
+        "kv_append_32k_rows": append_big,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)

@@ -155,6 +155,43 @@ mla_status mla_plan_device(const mla_decode_params* p, const int32_t* seq_lens, 
 mla_status mla_check_inputs_host(const mla_decode_params* p, const int32_t* block_table_host,
                                  const int32_t* seq_lens_host);
 
+/* ---- KV-cache append: the cache write that precedes each decode step,
+ * set_mla_kv_buffer(layer, out_cache_loc, k_nope, k_rope) in
+ * TRTLLMMLABackend.forward_decode on "sglang trtllm_mla_backend.py" and on
+ * "tokenspeed trtllm_mla.py".  Row i = [k_nope[i][0:512] | k_rope[i][0:64]]
+ * is stored in flat slot out_cache_loc[i] of the pool, that is page
+ * loc / page_size, slot loc % page_size (the token -> row map the decode
+ * reads through).  A bf16 pool stores the bf16 bits unchanged.  An fp8 pool
+ * stores the OCP float8_e4m3fn code of x / k_scale, computed as an fp32
+ * quotient, saturated to +-448 and rounded to nearest with ties to even
+ * (the per-tensor scale convention of scaled_fp8_quant in
+ * _quantize_fp8_qkv on "sglang trtllm_mla_backend.py"); a NaN stores 0x7F,
+ * an infinity saturates. */
+typedef struct {
+  int64_t nope_stride;        /* elements between rows of k_nope: >= 512, a multiple of 8 */
+  int64_t rope_stride;        /* elements between rows of k_rope: >= 64, a multiple of 8 */
+  int32_t num_tokens;         /* T >= 0 rows; T = 0 enqueues nothing */
+  int32_t kv_lora_rank;       /* must be 512 */
+  int32_t qk_rope_head_dim;   /* must be 64 */
+  int32_t page_size;          /* 32 or 64 */
+  int32_t num_pages;          /* pages in the pool, >= 1 */
+  int32_t kv_dtype;           /* an mla_kv_dtype: the pool's element type */
+  float k_scale;              /* fp8 pool: finite, > 0; bf16 pool: ignored */
+} mla_kv_append_params;
+
+/* Layouts:
+ *   k_nope        device, bf16  [T][nope_stride], 16-byte aligned (e.g. k[..., :512] of a [T][576] tensor)
+ *   k_rope        device, bf16  [T][rope_stride], 16-byte aligned (e.g. k[..., 512:])
+ *   out_cache_loc device, int64 [T] flat slots; a location outside
+ *                 [0, num_pages * page_size) is skipped (nothing is written for
+ *                 that row).  Locations should be distinct: with repeats, one of
+ *                 the rows is stored, which one is unspecified.
+ *   kv_pool       device, bf16 or e4m3fn [num_pages][page_size][576], 16-byte aligned (written)
+ * Enqueues one kernel on `stream` and returns without waiting.  Argument
+ * errors (MLA_ERR_INVALID_VALUE / MLA_ERR_NOT_SUPPORTED) enqueue nothing. */
+mla_status mla_kv_append(const mla_kv_append_params* p, const void* k_nope, const void* k_rope,
+                         const int64_t* out_cache_loc, void* kv_pool, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,12 @@ class mla_decode_params(ctypes.Structure):
         (n, ctypes.c_int32) for n in ("num_splits", "min_work_units", "num_cus")]
 
 
+class mla_kv_append_params(ctypes.Structure):
+    _fields_ = [("nope_stride", ctypes.c_int64), ("rope_stride", ctypes.c_int64)] + [
+        (n, ctypes.c_int32) for n in ("num_tokens", "kv_lora_rank", "qk_rope_head_dim", "page_size", "num_pages",
+                                      "kv_dtype")] + [("k_scale", ctypes.c_float)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -80,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.mla_plan_device.argtypes = [P, vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp]
         L.mla_check_inputs_host.restype = ctypes.c_int
         L.mla_check_inputs_host.argtypes = [P, vp, vp]
+        L.mla_kv_append.restype = ctypes.c_int
+        L.mla_kv_append.argtypes = [ctypes.POINTER(mla_kv_append_params), vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -241,6 +249,54 @@ def mla_check_inputs_host(p: mla_decode_params, block_table_host: np.ndarray, se
     sl = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
     return int(lib().mla_check_inputs_host(ctypes.byref(p), bt.ctypes.data_as(ctypes.c_void_p),
                                            sl.ctypes.data_as(ctypes.c_void_p)))
+
+
+def make_append_params(num_tokens: int, page_size: int, num_pages: int, kv_dtype: int = MLA_KV_BF16,
+                       k_scale: float = 1.0, nope_stride: int = LATENT_DIM, rope_stride: int = ROPE_DIM,
+                       kv_lora_rank: int = LATENT_DIM, qk_rope_head_dim: int = ROPE_DIM) -> mla_kv_append_params:
+    return mla_kv_append_params(int(nope_stride), int(rope_stride), int(num_tokens), int(kv_lora_rank),
+                                int(qk_rope_head_dim), int(page_size), int(num_pages), int(kv_dtype), float(k_scale))
+
+
+def mla_kv_append(k_nope, k_rope, out_cache_loc, kv_pool, *, k_scale: float = 1.0, stream=None,
+                  params: Optional[mla_kv_append_params] = None):
+    """Enqueue the cache write of T new rows on ``stream`` (default: torch's current stream).
+
+    k_nope [T, 512] and k_rope [T, 64] bf16 (rows may be strided, e.g. the two
+    slices of one [T, 576] tensor; elements contiguous); out_cache_loc int64
+    [T] flat slots page * page_size + slot; kv_pool [N, P, 576] bf16 or
+    float8_e4m3fn (written).  All on the GPU.  Returns kv_pool."""
+    import torch
+    for name, t in (("k_nope", k_nope), ("k_rope", k_rope), ("out_cache_loc", out_cache_loc), ("kv_pool", kv_pool)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    if k_nope.dtype != torch.bfloat16 or k_rope.dtype != torch.bfloat16:
+        raise ValueError("k_nope and k_rope must be bfloat16")
+    if out_cache_loc.dtype != torch.int64 or not out_cache_loc.is_contiguous():
+        raise ValueError("out_cache_loc must be contiguous int64")
+    if k_nope.dim() != 2 or k_rope.dim() != 2 or k_nope.shape[1] != LATENT_DIM or k_rope.shape[1] != ROPE_DIM:
+        raise ValueError("k_nope must be [T, 512] and k_rope [T, 64]")
+    if k_nope.stride(1) != 1 or k_rope.stride(1) != 1 or not kv_pool.is_contiguous():
+        raise ValueError("row elements must be contiguous, and the pool contiguous")
+    T = k_nope.shape[0]
+    if k_rope.shape[0] != T or out_cache_loc.numel() != T:
+        raise ValueError("k_nope, k_rope and out_cache_loc must have the same number of rows")
+    N, P, D = kv_pool.shape
+    if D != ROW_DIM:
+        raise ValueError("pool rows must be 576 wide")
+    fp8 = kv_pool.dtype in (torch.float8_e4m3fn, torch.uint8)
+    p = params if params is not None else make_append_params(
+        T, P, N, MLA_KV_FP8_E4M3FN if fp8 else MLA_KV_BF16, k_scale,
+        k_nope.stride(0) if T > 1 else LATENT_DIM, k_rope.stride(0) if T > 1 else ROPE_DIM)
+    _check(lib().mla_kv_append(ctypes.byref(p), _ptr(k_nope), _ptr(k_rope), _ptr(out_cache_loc), _ptr(kv_pool),
+                               _stream_handle(stream)), "mla_kv_append")
+    return kv_pool
+
+
+def append_work(num_tokens: int, kv_bytes: int) -> int:
+    """Bytes a KV append must move: each row's 576 bf16 inputs read, its 576
+    pool elements written, and its 8-byte location read."""
+    return int(num_tokens) * (ROW_DIM * 2 + ROW_DIM * kv_bytes + 8)
 
 
 def algorithmic_work(seq_lens: np.ndarray, q_len: int, heads: int, page_size: int, kv_bytes: int):

@@ -326,6 +326,42 @@ mla_status mla_plan_device(const mla_decode_params* p, const int32_t* seq_lens, 
   return MLA_OK;
 }
 
+mla_status mla_kv_append(const mla_kv_append_params* p, const void* k_nope, const void* k_rope,
+                         const int64_t* out_cache_loc, void* kv_pool, void* stream) {
+  if (p == nullptr) return MLA_ERR_INVALID_VALUE;
+  if (p->kv_lora_rank != mla::kLatentDim || p->qk_rope_head_dim != mla::kRowDim - mla::kLatentDim)
+    return MLA_ERR_NOT_SUPPORTED;
+  if (p->num_tokens < 0 || p->num_pages < 1) return MLA_ERR_INVALID_VALUE;
+  if (p->page_size != 32 && p->page_size != 64) return MLA_ERR_INVALID_VALUE;
+  if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP8_E4M3FN) return MLA_ERR_INVALID_VALUE;
+  if (p->kv_dtype == MLA_KV_FP8_E4M3FN && !finite_pos(p->k_scale)) return MLA_ERR_INVALID_VALUE;
+  if (p->nope_stride < mla::kLatentDim || p->rope_stride < mla::kRowDim - mla::kLatentDim ||
+      (p->nope_stride & 7) != 0 || (p->rope_stride & 7) != 0)
+    return MLA_ERR_INVALID_VALUE;
+  if (p->num_tokens == 0) return MLA_OK;
+  if (k_nope == nullptr || k_rope == nullptr || out_cache_loc == nullptr || kv_pool == nullptr)
+    return MLA_ERR_INVALID_VALUE;
+  if (((uintptr_t)k_nope | (uintptr_t)k_rope | (uintptr_t)kv_pool) & 15) return MLA_ERR_INVALID_VALUE;
+  if (((uintptr_t)out_cache_loc & 7) != 0) return MLA_ERR_INVALID_VALUE;
+  DeviceInfo di;
+  mla_status s = device_info(&di);
+  if (s != MLA_OK) return s;
+  if (!di.gfx950) return MLA_ERR_NOT_SUPPORTED;
+  mla::AppendArgs a;
+  a.nope = (const uint16_t*)k_nope;
+  a.rope = (const uint16_t*)k_rope;
+  a.loc = out_cache_loc;
+  a.pool = kv_pool;
+  a.nope_stride = p->nope_stride;
+  a.rope_stride = p->rope_stride;
+  a.slots = (int64_t)p->num_pages * p->page_size;
+  a.T = p->num_tokens;
+  a.fp8 = p->kv_dtype == MLA_KV_FP8_E4M3FN ? 1 : 0;
+  a.k_scale = a.fp8 ? p->k_scale : 1.f;
+  if (mla_launch_append(&a, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 mla_status mla_check_inputs_host(const mla_decode_params* p, const int32_t* block_table_host,
                                  const int32_t* seq_lens_host) {
   mla_status s = check_params(p);

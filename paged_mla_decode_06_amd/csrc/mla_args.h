@@ -32,6 +32,18 @@ struct CombineArgs {
   int64_t NG;   // groups of the plan
 };
 
+struct AppendArgs {
+  const uint16_t* nope;     // [T][nope_stride] bf16, first 512 elements of a row used
+  const uint16_t* rope;     // [T][rope_stride] bf16, first 64 used
+  const int64_t* loc;       // [T] flat slots page * P + slot
+  void* pool;               // [N * P][576] bf16 or e4m3fn
+  int64_t nope_stride, rope_stride;   // elements
+  int64_t slots;            // N * P
+  int32_t T;
+  int32_t fp8;
+  float k_scale;            // fp8: stored code = e4m3fn(x / k_scale)
+};
+
 }  // namespace mla
 
 extern "C" {
@@ -43,4 +55,5 @@ hipError_t mla_launch_gather(const void* pool, const int32_t* bt, const int32_t*
 hipError_t mla_launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t nrb, int32_t num_splits,
                            int64_t G, int32_t max_per_wg, int32_t* pieces, int32_t* counts, hipStream_t stream);
 size_t mla_split_lds_bytes(int32_t B, int32_t num_splits);
+hipError_t mla_launch_append(const mla::AppendArgs* a, hipStream_t stream);
 }

@@ -153,3 +153,58 @@ def test_algorithmic_work_formula():
     assert flops == 2 * 16 * 1088 * 357
     _, f4 = mla.algorithmic_work(np.array([10]), 4, 1, 64, 2)
     assert f4 == 2 * 1088 * (7 + 8 + 9 + 10)
+
+
+# ---- KV-cache append: argument checks before any device call
+def test_append_params_struct_layout():
+    # two int64 strides, 6 int32, 1 float, padded to 8 bytes
+    assert ctypes.sizeof(mla.mla_kv_append_params) == 48
+    assert "mla_kv_append" in mla.header_functions()
+
+
+def good_append(**kw):
+    base = dict(num_tokens=4, page_size=64, num_pages=8, kv_dtype=mla.MLA_KV_BF16, k_scale=1.0,
+                nope_stride=576, rope_stride=576)
+    base.update(kw)
+    return mla.make_append_params(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page_size=16), mla.MLA_ERR_INVALID_VALUE),
+    (dict(num_tokens=-1), mla.MLA_ERR_INVALID_VALUE),
+    (dict(num_pages=0), mla.MLA_ERR_INVALID_VALUE),
+    (dict(kv_dtype=3), mla.MLA_ERR_INVALID_VALUE),
+    (dict(kv_dtype=mla.MLA_KV_FP8_E4M3FN, k_scale=0.0), mla.MLA_ERR_INVALID_VALUE),
+    (dict(kv_dtype=mla.MLA_KV_FP8_E4M3FN, k_scale=float("inf")), mla.MLA_ERR_INVALID_VALUE),
+    (dict(nope_stride=511), mla.MLA_ERR_INVALID_VALUE),
+    (dict(nope_stride=580), mla.MLA_ERR_INVALID_VALUE),       # rows must stay 16-byte aligned
+    (dict(rope_stride=60), mla.MLA_ERR_INVALID_VALUE),
+    (dict(kv_lora_rank=256), mla.MLA_ERR_NOT_SUPPORTED),
+    (dict(qk_rope_head_dim=32), mla.MLA_ERR_NOT_SUPPORTED),
+])
+def test_append_invalid_params_rejected(L, kw, status):
+    p = good_append(**kw)
+    fake = ctypes.c_void_p(0x100000)
+    assert L.mla_kv_append(ctypes.byref(p), fake, fake, fake, fake, None) == status
+
+
+def test_append_null_and_alignment_checks(L):
+    p = good_append()
+    fake = ctypes.c_void_p(0x100000)
+    assert L.mla_kv_append(ctypes.byref(p), None, fake, fake, fake, None) == mla.MLA_ERR_INVALID_VALUE
+    assert L.mla_kv_append(ctypes.byref(p), fake, fake, fake, None, None) == mla.MLA_ERR_INVALID_VALUE
+    assert L.mla_kv_append(ctypes.byref(p), ctypes.c_void_p(0x100008), fake, fake, fake, None) == \
+        mla.MLA_ERR_INVALID_VALUE     # k_nope not 16-byte aligned
+    assert L.mla_kv_append(ctypes.byref(p), fake, fake, ctypes.c_void_p(0x100004), fake, None) == \
+        mla.MLA_ERR_INVALID_VALUE     # locations not 8-byte aligned
+    assert L.mla_kv_append(None, fake, fake, fake, fake, None) == mla.MLA_ERR_INVALID_VALUE
+
+
+def test_append_empty_is_a_noop(L):
+    p = good_append(num_tokens=0)
+    assert L.mla_kv_append(ctypes.byref(p), None, None, None, None, None) == mla.MLA_OK
+
+
+def test_append_work_formula():
+    assert mla.append_work(64, 2) == 64 * (1152 + 1152 + 8)
+    assert mla.append_work(10, 1) == 10 * (1152 + 576 + 8)
