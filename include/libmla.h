@@ -111,6 +111,35 @@ mla_status mla_decode(const mla_decode_params* p, const void* q, const void* kv_
                       const int32_t* seq_lens, void* out, float* lse, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* Where the two parts of the query live when they are not one [.., 576]
+ * row: query row (b, j, h), with token = b * q_len + j, has its 512-wide
+ * absorbed latent part at q_nope + token * nope_token_stride +
+ * h * nope_head_stride and its 64-wide rope part at q_rope +
+ * token * rope_token_stride + h * rope_head_stride (strides in bf16
+ * elements, each a multiple of 8, >= 0).  This is the pair the pages
+ * concatenate before the decode kernel (concat_mla_absorb_q_general(q_nope,
+ * q_rope) in TRTLLMMLABackend.forward_decode on "sglang
+ * trtllm_mla_backend.py"); for example the head-major output of the
+ * absorbed-query product viewed token-major has nope_token_stride = 512 and
+ * nope_head_stride = tokens * 512. */
+typedef struct {
+  int64_t nope_token_stride;
+  int64_t nope_head_stride;
+  int64_t rope_token_stride;
+  int64_t rope_head_stride;
+} mla_query_layout;
+
+/* mla_decode() with the query given as its two parts (see mla_query_layout)
+ * instead of one [B][q_len][H][576] tensor: the decode reads them in place,
+ * so no concatenated copy is made.  q_nope and q_rope: device, bf16, 16-byte
+ * aligned.  Results are bit-identical to mla_decode() on the concatenated
+ * query.  Other arguments, layouts and errors as mla_decode(); a stride that
+ * is negative or not a multiple of 8 is MLA_ERR_INVALID_VALUE. */
+mla_status mla_decode_qparts(const mla_decode_params* p, const void* q_nope, const void* q_rope,
+                             const mla_query_layout* layout, const void* kv_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* mla_decode() that also records three caller-created HIP events (hipEvent_t,
  * each may be NULL) on `stream`: before the split-KV kernel, between it and
  * the combine kernel, and after the combine, so that a benchmark can time the

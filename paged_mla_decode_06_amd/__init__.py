@@ -49,6 +49,11 @@ class mla_decode_params(ctypes.Structure):
         (n, ctypes.c_int32) for n in ("num_splits", "min_work_units", "num_cus")]
 
 
+class mla_query_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("nope_token_stride", "nope_head_stride", "rope_token_stride",
+                                             "rope_head_stride")]
+
+
 class mla_kv_append_params(ctypes.Structure):
     _fields_ = [("nope_stride", ctypes.c_int64), ("rope_stride", ctypes.c_int64)] + [
         (n, ctypes.c_int32) for n in ("num_tokens", "kv_lora_rank", "qk_rope_head_dim", "page_size", "num_pages",
@@ -86,6 +91,9 @@ def lib() -> ctypes.CDLL:
         L.mla_plan_device.argtypes = [P, vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp]
         L.mla_check_inputs_host.restype = ctypes.c_int
         L.mla_check_inputs_host.argtypes = [P, vp, vp]
+        L.mla_decode_qparts.restype = ctypes.c_int
+        L.mla_decode_qparts.argtypes = [P, vp, vp, ctypes.POINTER(mla_query_layout), vp, vp, vp, vp, vp, vp,
+                                        ctypes.c_size_t, vp]
         L.mla_kv_append.restype = ctypes.c_int
         L.mla_kv_append.argtypes = [ctypes.POINTER(mla_kv_append_params), vp, vp, vp, vp, vp]
         _lib = L
@@ -197,6 +205,60 @@ def mla_decode(q, kv_pool, block_table, seq_lens, out, lse=None, workspace=None,
                           _ptr(lse), _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                           _stream_handle(stream))
     _check(st, "mla_decode")
+    return out, lse
+
+
+def _token_head_strides(t, B: int, q_len: int, H: int, width: int, name: str):
+    """(token stride, head stride) of a query part given as [B, q_len, H, width]
+    or [B*q_len, H, width] with contiguous elements."""
+    if t.stride(-1) != 1 or t.shape[-1] != width:
+        raise ValueError(f"{name}: last dimension must be {width} contiguous elements")
+    if t.dim() == 4:
+        if tuple(t.shape[:3]) != (B, q_len, H) or (B > 1 and t.stride(0) != q_len * t.stride(1)):
+            raise ValueError(f"{name}: [B, q_len, H, {width}] with token rows b*q_len + j evenly strided")
+        return t.stride(1), t.stride(2)
+    if t.dim() == 3 and tuple(t.shape[:2]) == (B * q_len, H):
+        return t.stride(0), t.stride(1)
+    raise ValueError(f"{name}: expected [B, q_len, H, {width}] or [B*q_len, H, {width}]")
+
+
+def mla_decode_qparts(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse=None, workspace=None, *,
+                      max_seq_len: int, softmax_scale: float, k_scale: float = 1.0, num_splits: int = 0,
+                      min_work_units: int = 0, stream=None):
+    """mla_decode with the query as its latent part q_nope (512 wide) and rope
+    part q_rope (64 wide), each [B, q_len, H, w] or [B*q_len, H, w] with any
+    token and head strides (multiples of 8 elements): read in place, no
+    concatenation.  out [B, q_len, H, 512] fixes B, q_len and H."""
+    import torch
+    for name, t in (("q_nope", q_nope), ("q_rope", q_rope), ("kv_pool", kv_pool), ("block_table", block_table),
+                    ("seq_lens", seq_lens), ("out", out)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    if q_nope.dtype != torch.bfloat16 or q_rope.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise ValueError("q_nope, q_rope and out must be bfloat16")
+    if not (kv_pool.is_contiguous() and out.is_contiguous() and seq_lens.is_contiguous()):
+        raise ValueError("kv_pool, seq_lens and out must be contiguous")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or block_table.stride(-1) != 1:
+        raise ValueError("block_table and seq_lens must be int32 with contiguous rows")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32")
+    B, ql, H, Dv = out.shape
+    if Dv != LATENT_DIM:
+        raise ValueError("out must be [B, q_len, H, 512]")
+    nt, nh = _token_head_strides(q_nope, B, ql, H, LATENT_DIM, "q_nope")
+    rt, rh = _token_head_strides(q_rope, B, ql, H, ROPE_DIM, "q_rope")
+    N, P, Dk = kv_pool.shape
+    fp8 = kv_pool.dtype in (torch.float8_e4m3fn, torch.uint8)
+    p = make_params(B, ql, H, P, N, block_table.stride(0) if block_table.dim() == 2 else 1, max_seq_len,
+                    MLA_KV_FP8_E4M3FN if fp8 else MLA_KV_BF16, softmax_scale, k_scale, num_splits, min_work_units)
+    if workspace is None:
+        workspace = alloc_workspace(p, out.device)
+    lay = mla_query_layout(int(nt), int(nh), int(rt), int(rh))
+    st = lib().mla_decode_qparts(ctypes.byref(p), _ptr(q_nope), _ptr(q_rope), ctypes.byref(lay), _ptr(kv_pool),
+                                 _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace),
+                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                 _stream_handle(stream))
+    _check(st, "mla_decode_qparts")
     return out, lse
 
 

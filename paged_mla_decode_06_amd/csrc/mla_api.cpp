@@ -145,17 +145,43 @@ mla_status mla_decode_workspace_size(const mla_decode_params* p, size_t* bytes) 
   return MLA_OK;
 }
 
-static mla_status decode_impl(const mla_decode_params* p, const void* q, const void* kv_pool,
+// Where the query's two parts live: q_nope + token*nope_token_stride +
+// h*nope_head_stride (512 bf16) and q_rope + ... (64 bf16), token = b*q_len + j.
+struct QueryParts {
+  const void* nope;
+  const void* rope;
+  mla_query_layout s;
+};
+
+QueryParts merged_query(const mla_decode_params* p, const void* q) {
+  QueryParts qp;
+  qp.nope = q;
+  qp.rope = q == nullptr ? nullptr : (const void*)((const uint16_t*)q + kLatentDim);
+  qp.s.nope_token_stride = qp.s.rope_token_stride = (int64_t)p->num_heads * mla::kRowDim;
+  qp.s.nope_head_stride = qp.s.rope_head_stride = mla::kRowDim;
+  return qp;
+}
+
+static mla_status decode_impl(const mla_decode_params* p, const QueryParts& qp, const void* kv_pool,
                               const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream, void* ev_start,
                               void* ev_mid, void* ev_end) {
   mla_status s = check_params(p);
   if (s != MLA_OK) return s;
   if (p->batch == 0) return MLA_OK;
-  if (q == nullptr || kv_pool == nullptr || block_table == nullptr || seq_lens == nullptr || out == nullptr ||
-      workspace == nullptr)
+  if (qp.nope == nullptr || qp.rope == nullptr || kv_pool == nullptr || block_table == nullptr ||
+      seq_lens == nullptr || out == nullptr || workspace == nullptr)
     return MLA_ERR_INVALID_VALUE;
-  if (((uintptr_t)q | (uintptr_t)kv_pool | (uintptr_t)out) & 15) return MLA_ERR_INVALID_VALUE;
+  if (((uintptr_t)qp.nope | (uintptr_t)qp.rope | (uintptr_t)kv_pool | (uintptr_t)out) & 15)
+    return MLA_ERR_INVALID_VALUE;
+  {
+    // 16-byte aligned fragments need strides in whole multiples of 8 elements
+    const mla_query_layout& l = qp.s;
+    if (((l.nope_token_stride | l.nope_head_stride | l.rope_token_stride | l.rope_head_stride) & 7) != 0)
+      return MLA_ERR_INVALID_VALUE;
+    if (l.nope_token_stride < 0 || l.nope_head_stride < 0 || l.rope_token_stride < 0 || l.rope_head_stride < 0)
+      return MLA_ERR_INVALID_VALUE;
+  }
   if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_INVALID_VALUE;
   Layout lay;
   s = layout_of(p, &lay);
@@ -170,7 +196,12 @@ static mla_status decode_impl(const mla_decode_params* p, const void* q, const v
   const bool fp8 = p->kv_dtype == MLA_KV_FP8_E4M3FN;
   const float kscale = fp8 ? p->k_scale : 1.f;
   mla::SplitArgs a;
-  a.q = (const uint16_t*)q;
+  a.q = (const uint16_t*)qp.nope;
+  a.q_rope = (const uint16_t*)qp.rope;
+  a.qn_tok = qp.s.nope_token_stride;
+  a.qn_head = qp.s.nope_head_stride;
+  a.qr_tok = qp.s.rope_token_stride;
+  a.qr_head = qp.s.rope_head_stride;
   a.pool = kv_pool;
   a.bt = block_table;
   a.seq_lens = seq_lens;
@@ -221,7 +252,21 @@ static mla_status decode_impl(const mla_decode_params* p, const void* q, const v
 mla_status mla_decode(const mla_decode_params* p, const void* q, const void* kv_pool, const int32_t* block_table,
                       const int32_t* seq_lens, void* out, float* lse, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  return decode_impl(p, q, kv_pool, block_table, seq_lens, out, lse, workspace, workspace_bytes, stream, nullptr,
+  if (p == nullptr) return MLA_ERR_INVALID_VALUE;
+  return decode_impl(p, merged_query(p, q), kv_pool, block_table, seq_lens, out, lse, workspace, workspace_bytes,
+                     stream, nullptr, nullptr, nullptr);
+}
+
+mla_status mla_decode_qparts(const mla_decode_params* p, const void* q_nope, const void* q_rope,
+                             const mla_query_layout* layout, const void* kv_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (layout == nullptr) return MLA_ERR_INVALID_VALUE;
+  QueryParts qp;
+  qp.nope = q_nope;
+  qp.rope = q_rope;
+  qp.s = *layout;
+  return decode_impl(p, qp, kv_pool, block_table, seq_lens, out, lse, workspace, workspace_bytes, stream, nullptr,
                      nullptr, nullptr);
 }
 
@@ -229,8 +274,9 @@ mla_status mla_decode_timed(const mla_decode_params* p, const void* q, const voi
                             const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_split_done,
                             void* ev_end) {
-  return decode_impl(p, q, kv_pool, block_table, seq_lens, out, lse, workspace, workspace_bytes, stream, ev_start,
-                     ev_split_done, ev_end);
+  if (p == nullptr) return MLA_ERR_INVALID_VALUE;
+  return decode_impl(p, merged_query(p, q), kv_pool, block_table, seq_lens, out, lse, workspace, workspace_bytes,
+                     stream, ev_start, ev_split_done, ev_end);
 }
 
 mla_status mla_gather_kv(const mla_decode_params* p, const void* kv_pool, const int32_t* block_table,

@@ -6,7 +6,9 @@
 namespace mla {
 
 struct SplitArgs {
-  const uint16_t* q;        // [B][q_len][H][576] bf16
+  const uint16_t* q;        // latent part of query row (token, h): q + token*qn_tok + h*qn_head, 512 bf16
+  const uint16_t* q_rope;   // rope part: q_rope + token*qr_tok + h*qr_head, 64 bf16 (token = b*q_len + j)
+  int64_t qn_tok, qn_head, qr_tok, qr_head;   // element strides
   const void* pool;         // [N][P][576] bf16 or e4m3fn
   const int32_t* bt;        // [B][W]
   const int32_t* seq_lens;  // [B]

@@ -142,15 +142,16 @@ __device__ __forceinline__ int lds_off(int r, int c) {
 }
 
 // The 18 16-byte query fragments of one lane (dims 32k + 8(l/16) .. +8 of its
-// row, k < 18, at byte offsets 64k from p) in one asm statement that also
-// waits for them: nothing the compiler emits can touch the registers before
-// the data is there, and the compiler keeps no record of these loads, so it
+// row, k < 18): the 16 of the latent part at byte offsets 64k from pn, the
+// two of the rope part at 0 and 64 from pr.  One asm statement also waits
+// for them: nothing the compiler emits can touch the registers before the
+// data is there, and the compiler keeps no record of these loads, so it
 // never waits for them (and for every tile load behind them) inside the tile
 // loop.  The wait covers every vector memory operation issued before, which
 // is why the first tiles' loads are issued before this: their latency then
 // overlaps the query's.
 #define MLA_Q_OUT(k) "=&v"(q[k])
-__device__ __forceinline__ void load_q_fragments(u32x4_t (&q)[18], const void* p) {
+__device__ __forceinline__ void load_q_fragments(u32x4_t (&q)[18], const void* pn, const void* pr) {
   asm volatile(
       "global_load_dwordx4 %0, %18, off\n\t"
       "global_load_dwordx4 %1, %18, off offset:64\n\t"
@@ -168,13 +169,13 @@ __device__ __forceinline__ void load_q_fragments(u32x4_t (&q)[18], const void* p
       "global_load_dwordx4 %13, %18, off offset:832\n\t"
       "global_load_dwordx4 %14, %18, off offset:896\n\t"
       "global_load_dwordx4 %15, %18, off offset:960\n\t"
-      "global_load_dwordx4 %16, %18, off offset:1024\n\t"
-      "global_load_dwordx4 %17, %18, off offset:1088\n\t"
+      "global_load_dwordx4 %16, %19, off\n\t"
+      "global_load_dwordx4 %17, %19, off offset:64\n\t"
       "s_waitcnt vmcnt(0)"
       : MLA_Q_OUT(0), MLA_Q_OUT(1), MLA_Q_OUT(2), MLA_Q_OUT(3), MLA_Q_OUT(4), MLA_Q_OUT(5), MLA_Q_OUT(6),
         MLA_Q_OUT(7), MLA_Q_OUT(8), MLA_Q_OUT(9), MLA_Q_OUT(10), MLA_Q_OUT(11), MLA_Q_OUT(12), MLA_Q_OUT(13),
         MLA_Q_OUT(14), MLA_Q_OUT(15), MLA_Q_OUT(16), MLA_Q_OUT(17)
-      : "v"(p)
+      : "v"(pn), "v"(pr)
       : "memory");
 }
 #undef MLA_Q_OUT
@@ -702,9 +703,12 @@ __device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
   static_assert(kQSteps == 18, "load_q_fragments loads 18 fragments");
   bf16x8_t qf[kQSteps];
   {
-    const int64_t qrow_id = row_ok ? (int64_t)(b * a.q_len + jrow) * a.H + hrow : (int64_t)b * a.q_len * a.H;
+    // query token b*q_len + j, head h: the latent part and the rope part
+    // each through its own token and head strides
+    const int64_t tok = (int64_t)b * a.q_len + (row_ok ? jrow : 0);
+    const int64_t h = row_ok ? hrow : 0;
     u32x4_t qv[kQSteps];
-    load_q_fragments(qv, a.q + qrow_id * kRowDim + 8 * g);
+    load_q_fragments(qv, a.q + tok * a.qn_tok + h * a.qn_head + 8 * g, a.q_rope + tok * a.qr_tok + h * a.qr_head + 8 * g);
 #pragma unroll
     for (int k = 0; k < kQSteps; k++) qf[k] = __builtin_bit_cast(bf16x8_t, row_ok ? qv[k] : u32x4_t{0u, 0u, 0u, 0u});
   }

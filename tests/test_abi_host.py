@@ -208,3 +208,38 @@ def test_append_empty_is_a_noop(L):
 def test_append_work_formula():
     assert mla.append_work(64, 2) == 64 * (1152 + 1152 + 8)
     assert mla.append_work(10, 1) == 10 * (1152 + 576 + 8)
+
+
+# ---- query given as two parts: argument checks before any device call
+@pytest.mark.parametrize("strides,status", [
+    ((576 * 16, 576, 576 * 16, 576), None),               # the merged layout: gets past the checks
+    ((512, 512 * 2, 64, 64 * 16), None),
+    ((512 + 4, 512, 576, 576), mla.MLA_ERR_INVALID_VALUE),  # not a multiple of 8
+    ((576, 576, 576, 60), mla.MLA_ERR_INVALID_VALUE),
+    ((-576, 576, 576, 576), mla.MLA_ERR_INVALID_VALUE),
+])
+def test_qparts_stride_checks(L, strides, status):
+    p = good()
+    lay = mla.mla_query_layout(*strides)
+    fake = ctypes.c_void_p(0x100000)
+    ws = ctypes.c_void_p(0x200000)
+    st = L.mla_decode_qparts(ctypes.byref(p), fake, ctypes.c_void_p(0x300000), ctypes.byref(lay), fake, fake, fake,
+                             fake, None, ws, 1, None)
+    if status is None:
+        assert st == mla.MLA_ERR_WORKSPACE_TOO_SMALL      # every argument check passed
+    else:
+        assert st == status
+
+
+def test_qparts_null_and_alignment(L):
+    p = good()
+    lay = mla.mla_query_layout(576 * 16, 576, 576 * 16, 576)
+    fake = ctypes.c_void_p(0x100000)
+    ws = ctypes.c_void_p(0x200000)
+    big = 1 << 34
+    assert L.mla_decode_qparts(ctypes.byref(p), fake, fake, None, fake, fake, fake, fake, None, ws, big, None) == \
+        mla.MLA_ERR_INVALID_VALUE
+    assert L.mla_decode_qparts(ctypes.byref(p), fake, None, ctypes.byref(lay), fake, fake, fake, fake, None, ws, big,
+                               None) == mla.MLA_ERR_INVALID_VALUE
+    assert L.mla_decode_qparts(ctypes.byref(p), fake, ctypes.c_void_p(0x100408), ctypes.byref(lay), fake, fake, fake,
+                               fake, None, ws, big, None) == mla.MLA_ERR_INVALID_VALUE   # rope part misaligned
