@@ -55,6 +55,7 @@ class Workload:
     num_pages: Optional[int] = None   # None: ceil(1.25 * pages in use)
     k_scale: float = 1.0
     min_work_units: int = 0      # 0: let the planner size the grid to the CU count
+    ragged_q: bool = False       # per-request query lengths uniform in [1, q_len] (packed, see ragged())
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -69,6 +70,9 @@ WORKLOADS: Dict[str, Workload] = {
                  lens=("uniform", 2048, 8192)),
         Workload("fp8_kv", batch=256, q_len=1, heads=128, page_size=64, kv="fp8", seed=5,
                  lens=("uniform", 512, 4096), k_scale=0.5),
+        # the multi-token decode with a draft-extend batch's per-request query lengths
+        Workload("draft_extend", batch=128, q_len=4, heads=128, page_size=64, kv="bf16", seed=6,
+                 lens=("uniform", 2048, 8192), ragged_q=True),
     ]
 }
 
@@ -179,6 +183,35 @@ def generate(w: Workload | str, seed: Optional[int] = None, poison: bool = False
     if poison:
         poison_unused(inp)
     return inp
+
+
+@dataclasses.dataclass
+class Ragged:
+    """A ragged multi-token batch: request b's q_b query tokens are rows
+    qo_indptr[b] .. qo_indptr[b+1]-1 of the packed query (no padding)."""
+    base: Inputs             # pool, block table, seq_lens; base.q is the padded [B, q_max, H, 576] draw
+    q: np.ndarray            # uint16 bf16 bits [T, H, 576], T = qo_indptr[B]
+    qo_indptr: np.ndarray    # int32 [B+1]
+    q_lens: np.ndarray       # int32 [B]
+
+    @property
+    def total_q(self): return int(self.qo_indptr[-1])
+
+
+def ragged(inp: Inputs, q_lens: Optional[np.ndarray] = None, seed: Optional[int] = None) -> Ragged:
+    """Pack the first q_b query tokens of each request of ``inp`` (q_b drawn
+    uniform in [1, q_len] from ``seed`` unless given; seq_lens are taken to
+    count the q_b new tokens)."""
+    B, qmax, H, D = inp.q.shape
+    if q_lens is None:
+        rng = np.random.default_rng(inp.workload.seed + 1000 if seed is None else seed)
+        q_lens = rng.integers(1, qmax + 1, size=B)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    assert q_lens.shape == (B,) and (q_lens >= 0).all() and (q_lens <= qmax).all()
+    indptr = np.zeros(B + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum(q_lens)
+    q = np.concatenate([inp.q[b, :q_lens[b]] for b in range(B)]) if B else np.zeros((0, H, D), np.uint16)
+    return Ragged(inp, np.ascontiguousarray(q.reshape(-1, H, D)), indptr, q_lens)
 
 
 def poison_unused(inp: Inputs) -> None:
