@@ -140,6 +140,37 @@ mla_status mla_decode_qparts(const mla_decode_params* p, const void* q_nope, con
                              const int32_t* seq_lens, void* out, float* lse, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Ragged multi-token decode: request b has its own number of query tokens
+ * q_b = qo_indptr[b+1] - qo_indptr[b] (0 <= q_b <= p->q_len), stored as rows
+ * qo_indptr[b] .. qo_indptr[b+1]-1 of a packed query, with no padding -- the
+ * cu_seqlens_q form of the draft-extend batches of "tokenspeed
+ * trtllm_mla.py" (TRTLLMMLABackend.init_forward_metadata builds
+ * cu_seqlens_q from extend_seq_lens; the pages then pad every request to
+ * max_seq_len_q and unpad the output).  seq_lens[b] counts request b's q_b
+ * new tokens, and query token j of request b sees the tokens
+ * t < seq_lens[b] - q_b + 1 + j (the bottom-right alignment of mla_decode,
+ * per request).  p->q_len is the largest q_b (it sizes the plan and the
+ * workspace: mla_decode_workspace_size(p) applies unchanged).
+ *   q          device, bf16  [total_q_tokens][H][576]
+ *   qo_indptr  device, int32 [B+1], nondecreasing, qo_indptr[0] = 0,
+ *              qo_indptr[B] = total_q_tokens.  A request whose offsets
+ *              fall outside [0, total_q_tokens] or run backwards is treated
+ *              as having no query tokens (nothing is read or written for it).
+ *   out        device, bf16  [total_q_tokens][H][512]   (written)
+ *   lse        device, fp32  [total_q_tokens][H], or NULL
+ * Other arguments, layouts and errors as mla_decode().  With every q_b equal
+ * to p->q_len the results are bit-identical to mla_decode(). */
+mla_status mla_decode_ragged(const mla_decode_params* p, const void* q, const int32_t* qo_indptr,
+                             int32_t total_q_tokens, const void* kv_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Host-side check (CPU only) of a ragged batch's offsets: qo_indptr[0] = 0,
+ * 0 <= q_b <= p->q_len for every request, qo_indptr[B] = total_q_tokens.
+ * MLA_ERR_INVALID_VALUE on the first violation. */
+mla_status mla_check_qo_indptr_host(const mla_decode_params* p, const int32_t* qo_indptr_host,
+                                    int32_t total_q_tokens);
+
 /* mla_decode() that also records three caller-created HIP events (hipEvent_t,
  * each may be NULL) on `stream`: before the split-KV kernel, between it and
  * the combine kernel, and after the combine, so that a benchmark can time the

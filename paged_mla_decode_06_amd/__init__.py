@@ -94,6 +94,10 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_qparts.restype = ctypes.c_int
         L.mla_decode_qparts.argtypes = [P, vp, vp, ctypes.POINTER(mla_query_layout), vp, vp, vp, vp, vp, vp,
                                         ctypes.c_size_t, vp]
+        L.mla_decode_ragged.restype = ctypes.c_int
+        L.mla_decode_ragged.argtypes = [P, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.mla_check_qo_indptr_host.restype = ctypes.c_int
+        L.mla_check_qo_indptr_host.argtypes = [P, vp, ctypes.c_int32]
         L.mla_kv_append.restype = ctypes.c_int
         L.mla_kv_append.argtypes = [ctypes.POINTER(mla_kv_append_params), vp, vp, vp, vp, vp]
         _lib = L
@@ -262,6 +266,57 @@ def mla_decode_qparts(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse=N
     return out, lse
 
 
+def mla_decode_ragged(q, qo_indptr, kv_pool, block_table, seq_lens, out, lse=None, workspace=None, *,
+                      max_q_len: int, max_seq_len: int, softmax_scale: float, k_scale: float = 1.0,
+                      num_splits: int = 0, min_work_units: int = 0, stream=None,
+                      params: Optional[mla_decode_params] = None):
+    """Ragged multi-token decode: request b's query tokens are rows
+    qo_indptr[b] .. qo_indptr[b+1]-1 of the packed q [T, H, 576] bf16
+    (qo_indptr int32 [B+1] on the GPU, at most max_q_len per request); out
+    [T, H, 512] bf16, lse [T, H] fp32 or None.  Returns (out, lse)."""
+    import torch
+    for name, t in (("q", q), ("qo_indptr", qo_indptr), ("kv_pool", kv_pool), ("block_table", block_table),
+                    ("seq_lens", seq_lens), ("out", out)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    if not (q.is_contiguous() and kv_pool.is_contiguous() and out.is_contiguous() and seq_lens.is_contiguous()
+            and qo_indptr.is_contiguous()):
+        raise ValueError("q, qo_indptr, kv_pool, seq_lens and out must be contiguous")
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise ValueError("q and out must be bfloat16")
+    if qo_indptr.dtype != torch.int32 or block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("qo_indptr, block_table and seq_lens must be int32")
+    if block_table.stride(-1) != 1:
+        raise ValueError("block_table rows must be contiguous")
+    T, H, D = q.shape
+    if D != ROW_DIM or tuple(out.shape) != (T, H, LATENT_DIM):
+        raise ValueError("q must be [T, H, 576] and out [T, H, 512]")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (T, H)):
+        raise ValueError("lse must be contiguous float32 [T, H]")
+    B = seq_lens.numel()
+    if qo_indptr.numel() != B + 1:
+        raise ValueError("qo_indptr must hold B+1 offsets")
+    N, P, Dk = kv_pool.shape
+    fp8 = kv_pool.dtype in (torch.float8_e4m3fn, torch.uint8)
+    p = params if params is not None else make_params(
+        B, max_q_len, H, P, N, block_table.stride(0) if block_table.dim() == 2 else 1, max_seq_len,
+        MLA_KV_FP8_E4M3FN if fp8 else MLA_KV_BF16, softmax_scale, k_scale, num_splits, min_work_units)
+    if workspace is None:
+        workspace = alloc_workspace(p, q.device)
+    st = lib().mla_decode_ragged(ctypes.byref(p), _ptr(q), _ptr(qo_indptr), int(T), _ptr(kv_pool),
+                                 _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace),
+                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                 _stream_handle(stream))
+    _check(st, "mla_decode_ragged")
+    return out, lse
+
+
+def mla_check_qo_indptr_host(p: mla_decode_params, qo_indptr_host: np.ndarray, total_q_tokens: int) -> int:
+    a = np.ascontiguousarray(qo_indptr_host, dtype=np.int32)
+    return int(lib().mla_check_qo_indptr_host(ctypes.byref(p), a.ctypes.data_as(ctypes.c_void_p),
+                                              int(total_q_tokens)))
+
+
 def mla_decode_timed(p: mla_decode_params, q, kv_pool, block_table, seq_lens, out, lse, workspace, stream,
                      ev_start, ev_split_done, ev_end):
     """mla_decode with raw hipEvent_t handles (ints, or None) recorded around the two kernels."""
@@ -359,6 +414,19 @@ def append_work(num_tokens: int, kv_bytes: int) -> int:
     """Bytes a KV append must move: each row's 576 bf16 inputs read, its 576
     pool elements written, and its 8-byte location read."""
     return int(num_tokens) * (ROW_DIM * 2 + ROW_DIM * kv_bytes + 8)
+
+
+def algorithmic_work_ragged(seq_lens: np.ndarray, q_lens: np.ndarray, heads: int, page_size: int, kv_bytes: int):
+    """(bytes, flops) of a ragged decode: as algorithmic_work, with request b's
+    own q_b query tokens (vis(j) = L_b - q_b + 1 + j)."""
+    L = np.maximum(np.asarray(seq_lens, dtype=np.int64), 0)
+    qb = np.asarray(q_lens, dtype=np.int64)
+    n_pages = (L + page_size - 1) // page_size
+    rows = int(qb.sum()) * heads
+    nbytes = int(L.sum()) * ROW_DIM * kv_bytes + rows * (ROW_DIM * 2 + LATENT_DIM * 2 + 4) \
+        + 4 * int(n_pages.sum()) + 4 * L.shape[0] + 4 * (L.shape[0] + 1)
+    vis = sum(int(np.maximum(L[b] - qb[b] + 1 + np.arange(qb[b]), 0).sum()) for b in range(L.shape[0]))
+    return nbytes, 2 * heads * (ROW_DIM + LATENT_DIM) * vis
 
 
 def algorithmic_work(seq_lens: np.ndarray, q_len: int, heads: int, page_size: int, kv_bytes: int):

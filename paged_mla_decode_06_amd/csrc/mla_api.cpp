@@ -119,6 +119,29 @@ mla_status layout_of(const mla_decode_params* p, Layout* lay) {
 
 }  // namespace
 
+namespace {
+
+// Where the query's two parts live: q_nope + token*nope_token_stride +
+// h*nope_head_stride (512 bf16) and q_rope + ... (64 bf16), token = b*q_len + j.
+struct QueryParts {
+  const void* nope;
+  const void* rope;
+  mla_query_layout s;
+  const int32_t* qo_indptr = nullptr;   // ragged batch: per-request query token offsets [B+1]
+  int32_t total_q = 0;                  // ragged batch: query tokens in q and out
+};
+
+QueryParts merged_query(const mla_decode_params* p, const void* q) {
+  QueryParts qp;
+  qp.nope = q;
+  qp.rope = q == nullptr ? nullptr : (const void*)((const uint16_t*)q + kLatentDim);
+  qp.s.nope_token_stride = qp.s.rope_token_stride = (int64_t)p->num_heads * mla::kRowDim;
+  qp.s.nope_head_stride = qp.s.rope_head_stride = mla::kRowDim;
+  return qp;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
@@ -143,23 +166,6 @@ mla_status mla_decode_workspace_size(const mla_decode_params* p, size_t* bytes) 
   if (s != MLA_OK) return s;
   *bytes = lay.total;
   return MLA_OK;
-}
-
-// Where the query's two parts live: q_nope + token*nope_token_stride +
-// h*nope_head_stride (512 bf16) and q_rope + ... (64 bf16), token = b*q_len + j.
-struct QueryParts {
-  const void* nope;
-  const void* rope;
-  mla_query_layout s;
-};
-
-QueryParts merged_query(const mla_decode_params* p, const void* q) {
-  QueryParts qp;
-  qp.nope = q;
-  qp.rope = q == nullptr ? nullptr : (const void*)((const uint16_t*)q + kLatentDim);
-  qp.s.nope_token_stride = qp.s.rope_token_stride = (int64_t)p->num_heads * mla::kRowDim;
-  qp.s.nope_head_stride = qp.s.rope_head_stride = mla::kRowDim;
-  return qp;
 }
 
 static mla_status decode_impl(const mla_decode_params* p, const QueryParts& qp, const void* kv_pool,
@@ -202,6 +208,8 @@ static mla_status decode_impl(const mla_decode_params* p, const QueryParts& qp, 
   a.qn_head = qp.s.nope_head_stride;
   a.qr_tok = qp.s.rope_token_stride;
   a.qr_head = qp.s.rope_head_stride;
+  a.qo_indptr = qp.qo_indptr;
+  a.total_q = qp.qo_indptr != nullptr ? qp.total_q : p->batch * p->q_len;
   a.pool = kv_pool;
   a.bt = block_table;
   a.seq_lens = seq_lens;
@@ -235,6 +243,8 @@ static mla_status decode_impl(const mla_decode_params* p, const QueryParts& qp, 
     c.seq_lens = seq_lens;
     c.out = a.out;
     c.lse = lse;
+    c.qo_indptr = a.qo_indptr;
+    c.total_q = a.total_q;
     c.B = a.B;
     c.q_len = a.q_len;
     c.H = a.H;
@@ -255,6 +265,38 @@ mla_status mla_decode(const mla_decode_params* p, const void* q, const void* kv_
   if (p == nullptr) return MLA_ERR_INVALID_VALUE;
   return decode_impl(p, merged_query(p, q), kv_pool, block_table, seq_lens, out, lse, workspace, workspace_bytes,
                      stream, nullptr, nullptr, nullptr);
+}
+
+mla_status mla_decode_ragged(const mla_decode_params* p, const void* q, const int32_t* qo_indptr,
+                             int32_t total_q_tokens, const void* kv_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (p == nullptr) return MLA_ERR_INVALID_VALUE;
+  if (total_q_tokens < 0 || (p->batch > 0 && qo_indptr == nullptr)) return MLA_ERR_INVALID_VALUE;
+  if ((((uintptr_t)qo_indptr) & 3) != 0) return MLA_ERR_INVALID_VALUE;
+  QueryParts qp;
+  qp.nope = q;
+  qp.rope = q == nullptr ? nullptr : (const void*)((const uint16_t*)q + kLatentDim);
+  qp.s.nope_token_stride = qp.s.rope_token_stride = (int64_t)p->num_heads * mla::kRowDim;
+  qp.s.nope_head_stride = qp.s.rope_head_stride = mla::kRowDim;
+  qp.qo_indptr = qo_indptr;
+  qp.total_q = total_q_tokens;
+  return decode_impl(p, qp, kv_pool, block_table, seq_lens, out, lse, workspace, workspace_bytes, stream, nullptr,
+                     nullptr, nullptr);
+}
+
+mla_status mla_check_qo_indptr_host(const mla_decode_params* p, const int32_t* qo_indptr_host,
+                                    int32_t total_q_tokens) {
+  mla_status s = check_params(p);
+  if (s != MLA_OK) return s;
+  if (p->batch > 0 && qo_indptr_host == nullptr) return MLA_ERR_INVALID_VALUE;
+  if (p->batch > 0 && qo_indptr_host[0] != 0) return MLA_ERR_INVALID_VALUE;
+  for (int32_t b = 0; b < p->batch; b++) {
+    const int32_t n = qo_indptr_host[b + 1] - qo_indptr_host[b];
+    if (n < 0 || n > p->q_len) return MLA_ERR_INVALID_VALUE;
+  }
+  if (p->batch > 0 && qo_indptr_host[p->batch] != total_q_tokens) return MLA_ERR_INVALID_VALUE;
+  return MLA_OK;
 }
 
 mla_status mla_decode_qparts(const mla_decode_params* p, const void* q_nope, const void* q_rope,

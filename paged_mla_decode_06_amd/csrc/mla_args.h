@@ -17,6 +17,8 @@ struct SplitArgs {
   uint16_t* part_o;         // [slots][64][512] bf16, normalised partial outputs
   float* part_lse;          // [slots][64]
   int32_t* pos_off_ws;      // [B+1] cost-position offsets (balanced mode), written by workgroup 0
+  const int32_t* qo_indptr;  // ragged batch: request b's query tokens are [qo_indptr[b], qo_indptr[b+1]); null: b*q_len + j
+  int32_t total_q;          // ragged batch: query tokens in q / out (bounds the offsets)
   int32_t B, q_len, H, P, W, N, max_seq_len, nrb, R, num_splits;
   int64_t NG;   // groups of the plan
   float scale_log2;         // softmax_scale * (k_scale for fp8) * log2(e)
@@ -30,6 +32,8 @@ struct CombineArgs {
   const int32_t* seq_lens;
   uint16_t* out;
   float* lse;
+  const int32_t* qo_indptr;
+  int32_t total_q;
   int32_t B, q_len, H, nrb, R, max_seq_len, num_splits;
   int64_t NG;   // groups of the plan
 };

@@ -141,6 +141,24 @@ __device__ __forceinline__ int lds_off(int r, int c) {
   return r * kRowBytes + (((c & ~7) | ((c & 7) ^ swz(r))) << 4);
 }
 
+// The query tokens of request b: the index of the first one and their
+// number q_b.  A uniform batch has q_b = q_len at b*q_len; a ragged batch
+// reads them from its offsets, and a request whose offsets fall outside
+// [0, total_q] or run backwards gets none (so a bad offset never moves a read
+// or a write out of the query and output tensors).  q_b is at most q_len, the
+// bound the plan was sized for.
+struct QExtent {
+  int64_t tok0;
+  int32_t qb;
+};
+template <bool RAGGED, class Args>
+__device__ __forceinline__ QExtent q_extent(const Args& a, int32_t b) {
+  if (!RAGGED || a.qo_indptr == nullptr) return QExtent{(int64_t)b * a.q_len, a.q_len};
+  const int32_t s = a.qo_indptr[b], e = a.qo_indptr[b + 1];
+  if (s < 0 || e < s || e > a.total_q) return QExtent{0, 0};
+  return QExtent{(int64_t)s, e - s < a.q_len ? e - s : a.q_len};
+}
+
 // The 18 16-byte query fragments of one lane (dims 32k + 8(l/16) .. +8 of its
 // row, k < 18): the 16 of the latent part at byte offsets 64k from pn, the
 // two of the rope part at 0 and 64 from pr.  One asm statement also waits
@@ -681,7 +699,7 @@ __device__ void load_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, c
 
 // The QK waves' side of one piece: the scores and the online softmax of the
 // wave's 16 rows.
-template <bool FP8>
+template <bool FP8, bool RAGGED>
 __device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& lo_, const Piece& pc, int w) {
   const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
   const int b = pc.b;
@@ -690,9 +708,10 @@ __device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
   const int nt = pc.tile1 - pc.tile0;
   const int rib = 16 * w + i16;   // this lane's row in the block
   const int row = pc.rb * kRowsPerBlock + rib;
-  const bool row_ok = row < a.R;
+  const QExtent qe = q_extent<RAGGED>(a, b);
+  const bool row_ok = row < qe.qb * a.H;
   const int jrow = row_ok ? row / a.H : 0, hrow = row_ok ? row - jrow * a.H : 0;
-  const int limit = min(tok_end, L - a.q_len + 1 + jrow);   // tokens t < limit are visible to this row
+  const int limit = min(tok_end, L - qe.qb + 1 + jrow);   // tokens t < limit are visible to this row
   // smallest limit over the wave's rows: tiles below it need no mask
   int lim_min = limit;
 #pragma unroll
@@ -705,7 +724,7 @@ __device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
   {
     // query token b*q_len + j, head h: the latent part and the rope part
     // each through its own token and head strides
-    const int64_t tok = (int64_t)b * a.q_len + (row_ok ? jrow : 0);
+    const int64_t tok = qe.tok0 + (row_ok ? jrow : 0);
     const int64_t h = row_ok ? hrow : 0;
     u32x4_t qv[kQSteps];
     load_q_fragments(qv, a.q + tok * a.qn_tok + h * a.qn_head + 8 * g, a.q_rope + tok * a.qr_tok + h * a.qr_head + 8 * g);
@@ -740,7 +759,7 @@ __device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
 
 // The PV waves' side of one piece: the output rows, written with the LSE (or
 // as a partial result).
-template <bool FP8>
+template <bool FP8, bool RAGGED>
 __device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& lo_, const Piece& pc, int v) {
   const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
   const int b = pc.b;
@@ -791,16 +810,18 @@ __device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
   // Wave v copies out rows kCopyRows*v .. +kCopyRows and their LSEs: lane l
   // carries bytes 16l .. 16l+15 of a row.
   constexpr int kCopyRows = kRowsPerBlock / kPVWaves;
+  const QExtent qe = q_extent<RAGGED>(a, b);
+  const int R_b = qe.qb * a.H;
   {
     const int rib = kCopyRows * v + i16;
     const int row = pc.rb * kRowsPerBlock + rib;
-    if (row < a.R && g == 0 && i16 < kCopyRows) {
+    if (row < R_b && g == 0 && i16 < kCopyRows) {
       const float m_run = stats[2 * rib], l_tot = stats[2 * rib + 1];
       const float lse_nat = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
       if (pc.slot < 0) {
         if (a.lse != nullptr) {
           const int jq = row / a.H;
-          a.lse[(int64_t)(b * a.q_len + jq) * a.H + (row - jq * a.H)] = lse_nat;
+          a.lse[(qe.tok0 + jq) * a.H + (row - jq * a.H)] = lse_nat;
         }
       } else {
         a.part_lse[(int64_t)pc.slot * kRowsPerBlock + rib] = lse_nat;
@@ -810,12 +831,12 @@ __device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
   for (int rr = 0; rr < kCopyRows; rr++) {
     const int r_in = kCopyRows * v + rr;
     const int r = pc.rb * kRowsPerBlock + r_in;
-    if (r >= a.R) break;
+    if (r >= R_b) break;
     const u32x4_t o = *(__attribute__((address_space(3))) const u32x4_t*)(lds + r_in * kStagePitch + 16 * lane);
     uint16_t* dst;
     if (pc.slot < 0) {
       const int jq = r / a.H;
-      dst = a.out + ((int64_t)(b * a.q_len + jq) * a.H + (r - jq * a.H)) * kLatentDim;
+      dst = a.out + ((qe.tok0 + jq) * a.H + (r - jq * a.H)) * kLatentDim;
     } else {
       dst = a.part_o + ((int64_t)pc.slot * kRowsPerBlock + r_in) * kLatentDim;
     }
@@ -919,9 +940,15 @@ __device__ __forceinline__ int32_t find_request(const int32_t* off, int32_t B, i
 
 // Every wave of a workgroup walks the same pieces: the loader waves fill the
 // tile ring, the compute waves consume it; their barriers pair up one to one.
-template <bool FP8, class PieceFn>
+template <bool FP8, bool RAGGED, class PieceFn>
 __device__ __forceinline__ void for_each_piece(const SplitArgs& a, int64_t grp, int32_t rb, int32_t total,
-                                               int32_t b_first, int32_t off_first, PieceFn&& fn) {
+                                               int32_t b_first, int32_t off_first, PieceFn&& fn_all) {
+  // A ragged batch's request with fewer query rows than this row block's
+  // first has nothing here: every wave of the workgroup skips the piece.
+  auto fn = [&](const Piece& pc) {
+    if (RAGGED && pc.rb * kRowsPerBlock >= q_extent<RAGGED>(a, pc.b).qb * a.H) return;
+    fn_all(pc);
+  };
   if (a.num_splits > 0) {
     const int32_t b = (int32_t)(grp / a.num_splits);
     const int32_t U = units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
@@ -933,7 +960,9 @@ __device__ __forceinline__ void for_each_piece(const SplitArgs& a, int64_t grp, 
   balanced_pieces(grp, a.NG, rb, a.nrb, total, b_first, off_first, units, fn);
 }
 
-template <bool FP8>
+// RAGGED: per-request query lengths from a.qo_indptr (a separate
+// instantiation, so the uniform batch's code is what it was without them).
+template <bool FP8, bool RAGGED>
 __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   lds_char* tiles = (lds_char*)smem;
@@ -975,19 +1004,19 @@ __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a
     const int lw = wave - kLoaderWave0;
     Stage<FP8> stg;
     stg.init(lw);
-    for_each_piece<FP8>(a, grp, rb, total, b_first, off_first,
-                        [&](const Piece& pc) { load_piece<FP8>(a, tiles, stg, pc, lw); });
+    for_each_piece<FP8, RAGGED>(a, grp, rb, total, b_first, off_first,
+                                [&](const Piece& pc) { load_piece<FP8>(a, tiles, stg, pc, lw); });
   } else if (wave >= kPVWave0) {
     LaneOffsets lo_;
     lo_.init();
-    for_each_piece<FP8>(a, grp, rb, total, b_first, off_first,
-                        [&](const Piece& pc) { pv_piece<FP8>(a, tiles, lo_, pc, wave - kPVWave0); });
+    for_each_piece<FP8, RAGGED>(a, grp, rb, total, b_first, off_first,
+                                [&](const Piece& pc) { pv_piece<FP8, RAGGED>(a, tiles, lo_, pc, wave - kPVWave0); });
   } else {
     if (MLA_PRIO_QK) __builtin_amdgcn_s_setprio(MLA_PRIO_QK);
     LaneOffsets lo_;
     lo_.init();
-    for_each_piece<FP8>(a, grp, rb, total, b_first, off_first,
-                        [&](const Piece& pc) { qk_piece<FP8>(a, tiles, lo_, pc, wave - kQKWave0); });
+    for_each_piece<FP8, RAGGED>(a, grp, rb, total, b_first, off_first,
+                                [&](const Piece& pc) { qk_piece<FP8, RAGGED>(a, tiles, lo_, pc, wave - kQKWave0); });
   }
 }
 
@@ -1005,7 +1034,8 @@ __global__ __launch_bounds__(kThreads, 8) void mla_combine_kernel(CombineArgs a)
   const int row_in_blk = (int)(blockIdx.x - blk * chunks) * kCombineRowsPerBlock + wave;
   const int32_t b = (int32_t)(blk / a.nrb), rb = (int32_t)(blk - (int64_t)b * a.nrb);
   const int row = rb * kRowsPerBlock + row_in_blk;
-  if (row >= a.R) return;
+  const QExtent qe = q_extent<true>(a, b);
+  if (row >= qe.qb * a.H) return;
   const int32_t U = units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
   // the pieces of this row block: groups [g0, g1]
   int64_t g0, g1, first_pos = 0, total = 0;
@@ -1107,7 +1137,7 @@ __global__ __launch_bounds__(kThreads, 8) void mla_combine_kernel(CombineArgs a)
   for (int d = 32; d >= 1; d >>= 1) den += __shfl_xor(den, d);
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int32_t jq = row / a.H, h = row - jq * a.H;
-  const int64_t orow = (int64_t)(b * a.q_len + jq) * a.H + h;
+  const int64_t orow = (qe.tok0 + jq) * a.H + h;
   u32x4_t w;
 #pragma unroll
   for (int e = 0; e < 4; e++)
@@ -1185,21 +1215,22 @@ size_t mla_split_lds_bytes(int32_t B, int32_t num_splits) {
 
 hipError_t mla_launch_split(const mla::SplitArgs* a, int fp8, hipStream_t stream) {
   const size_t lds = mla_split_lds_bytes(a->B, a->num_splits);
-  static bool attr_set[2] = {false, false};
-  if (!attr_set[fp8 ? 1 : 0]) {
+  const bool ragged = a->qo_indptr != nullptr;
+  const int v = (fp8 ? 1 : 0) + (ragged ? 2 : 0);
+  void (*const fns[4])(mla::SplitArgs) = {mla::mla_split_kernel<false, false>, mla::mla_split_kernel<true, false>,
+                                          mla::mla_split_kernel<false, true>, mla::mla_split_kernel<true, true>};
+  static bool attr_set[4] = {false, false, false, false};
+  if (!attr_set[v]) {
     // dynamic LDS above 64 KB: raise the per-kernel limit once to what the
     // kernel uses (static and dynamic LDS together stay within the 160 KB a
     // gfx950 workgroup may have)
-    const void* fn = fp8 ? (const void*)mla::mla_split_kernel<true> : (const void*)mla::mla_split_kernel<false>;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)mla::kSplitLdsBytes);
+    hipError_t e = hipFuncSetAttribute((const void*)fns[v], hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)mla::kSplitLdsBytes);
     if (e != hipSuccess) return e;
-    attr_set[fp8 ? 1 : 0] = true;
+    attr_set[v] = true;
   }
   const unsigned grid = (unsigned)mla::launch_grid(a->NG, a->nrb);
-  if (fp8)
-    hipLaunchKernelGGL(mla::mla_split_kernel<true>, dim3(grid), dim3(mla::kSplitThreads), lds, stream, *a);
-  else
-    hipLaunchKernelGGL(mla::mla_split_kernel<false>, dim3(grid), dim3(mla::kSplitThreads), lds, stream, *a);
+  hipLaunchKernelGGL(fns[v], dim3(grid), dim3(mla::kSplitThreads), lds, stream, *a);
   return hipGetLastError();
 }
 

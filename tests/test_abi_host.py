@@ -243,3 +243,32 @@ def test_qparts_null_and_alignment(L):
                                None) == mla.MLA_ERR_INVALID_VALUE
     assert L.mla_decode_qparts(ctypes.byref(p), fake, ctypes.c_void_p(0x100408), ctypes.byref(lay), fake, fake, fake,
                                fake, None, ws, big, None) == mla.MLA_ERR_INVALID_VALUE   # rope part misaligned
+
+
+# ---- ragged batches: host checks
+def test_qo_indptr_host_check():
+    p = good(batch=3, q_len=4)
+    assert mla.mla_check_qo_indptr_host(p, np.array([0, 2, 2, 6]), 6) == mla.MLA_OK
+    assert mla.mla_check_qo_indptr_host(p, np.array([1, 2, 2, 6]), 6) == mla.MLA_ERR_INVALID_VALUE   # not from 0
+    assert mla.mla_check_qo_indptr_host(p, np.array([0, 3, 2, 6]), 6) == mla.MLA_ERR_INVALID_VALUE   # backwards
+    assert mla.mla_check_qo_indptr_host(p, np.array([0, 5, 6, 7]), 7) == mla.MLA_ERR_INVALID_VALUE   # q_b > q_len
+    assert mla.mla_check_qo_indptr_host(p, np.array([0, 2, 2, 6]), 7) == mla.MLA_ERR_INVALID_VALUE   # total
+
+
+def test_ragged_argument_checks(L):
+    p = good()
+    fake = ctypes.c_void_p(0x100000)
+    ws = ctypes.c_void_p(0x200000)
+    assert L.mla_decode_ragged(ctypes.byref(p), fake, None, 2, fake, fake, fake, fake, None, ws, 1 << 34,
+                               None) == mla.MLA_ERR_INVALID_VALUE      # no offsets
+    assert L.mla_decode_ragged(ctypes.byref(p), fake, fake, -1, fake, fake, fake, fake, None, ws, 1 << 34,
+                               None) == mla.MLA_ERR_INVALID_VALUE      # negative token count
+    assert L.mla_decode_ragged(ctypes.byref(p), fake, fake, 2, fake, fake, fake, fake, None, ws, 1,
+                               None) == mla.MLA_ERR_WORKSPACE_TOO_SMALL  # every argument check passed
+
+
+def test_ragged_algorithmic_work():
+    nb, fl = mla.algorithmic_work_ragged(np.array([10, 20]), np.array([1, 3]), 2, 32, 2)
+    nu, fu = mla.algorithmic_work(np.array([10]), 1, 2, 32, 2)
+    assert fl == 2 * 2 * 1088 * (10 + 18 + 19 + 20)
+    assert nb == 30 * 1152 + 4 * 2 * (1152 + 1024 + 4) + 4 * 2 + 8 + 12

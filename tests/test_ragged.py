@@ -1,0 +1,94 @@
+"""GPU ragged multi-token decode (mla_decode_ragged) vs the CPU oracle, through
+the C ABI: per-request query lengths packed by offsets, including requests
+with no query token; bit-identical to mla_decode when every length is the
+same; offsets outside the query tensor are ignored, not followed."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import paged_mla_decode_06_amd as mla
+import oracle
+from oracle import ragged as RG
+import oracle_pins as P
+from mla_synth import generate, ragged
+import gpu_util as G
+
+
+def run_ragged(rg, total_q=None, guard=0, **kw):
+    inp = rg.base
+    _, pool, bt, sl = G.to_device(inp)
+    T, H, _ = rg.q.shape
+    q = torch.from_numpy(rg.q.view(np.int16)).view(torch.bfloat16).cuda()
+    ind = torch.from_numpy(rg.qo_indptr).cuda()
+    out_full = torch.full((T + guard, H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse_full = torch.full((T + guard, H), float("nan"), dtype=torch.float32, device="cuda")
+    Tq = T if total_q is None else total_q
+    q_use = q if total_q is None else q[:total_q]
+    args = dict(max_q_len=inp.q_len, max_seq_len=inp.max_seq_len, softmax_scale=inp.softmax_scale,
+                k_scale=inp.k_scale, min_work_units=inp.workload.min_work_units)
+    args.update(kw)
+    mla.mla_decode_ragged(q_use.contiguous(), ind, pool, bt, sl, out_full[:Tq], lse_full[:Tq], **args)
+    torch.cuda.synchronize()
+    return out_full.float().cpu().numpy(), lse_full.cpu().numpy()
+
+
+CASES = [
+    # kv, q_max, heads, page, lens, q_lens
+    ("bf16", 4, 128, 64, (4, 5, 67, 300, 130), (1, 4, 2, 3, 4)),
+    ("bf16", 4, 16, 32, (1, 2, 3, 40, 64, 65), (1, 2, 0, 4, 3, 1)),
+    ("bf16", 3, 40, 64, (2, 3, 97), (3, 1, 2)),
+    ("bf16", 8, 16, 32, (8, 100, 33), (8, 5, 1)),
+    ("fp8", 4, 32, 64, (4, 70, 131, 0), (2, 4, 1, 0)),
+    ("fp8", 2, 128, 32, (5, 300), (2, 1)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("mode", ["balanced", "balanced8", "split3"])
+def test_small_cases(case, mode):
+    kv, qmax, H, Pg, lens, qls = CASES[case]
+    inp = P.small(kv=kv, q_len=qmax, heads=H, page_size=Pg, lens=lens, seed=200 + case)
+    rg = ragged(inp, q_lens=qls)
+    kw = dict(balanced=dict(), balanced8=dict(min_work_units=8), split3=dict(num_splits=3))[mode]
+    o, l = run_ragged(rg, **kw)
+    ro, rl = RG.decode(oracle.default(), rg)
+    G.compare(o, l, ro, rl, fp8=kv == "fp8", what=f"{CASES[case]} {mode}")
+
+
+def test_uniform_lengths_identical_to_mla_decode():
+    inp = P.small(kv="bf16", q_len=4, heads=128, page_size=64, lens=(4, 67, 300, 1000), seed=210)
+    rg = ragged(inp, q_lens=[4, 4, 4, 4])
+    o, l = run_ragged(rg)
+    uo, ul = G.run(inp)
+    assert np.array_equal(o.reshape(uo.shape).view(np.uint32), uo.view(np.uint32))
+    assert np.array_equal(l.reshape(ul.shape).view(np.uint32), ul.view(np.uint32))
+
+
+def test_offsets_past_the_query_are_ignored():
+    """total_q below the last offset: the last request is treated as having no
+    query token; nothing is written past row total_q (guard rows stay NaN)."""
+    inp = P.small(kv="bf16", q_len=3, heads=16, page_size=32, lens=(10, 40, 70), seed=211)
+    rg = ragged(inp, q_lens=[2, 3, 3])
+    o, l = run_ragged(rg, total_q=5, guard=3)
+    ro, rl = RG.decode(oracle.default(), rg)
+    G.compare(o[:5], l[:5], ro[:5], rl[:5], what="first two requests")
+    assert np.isnan(o[5:]).all() and np.isnan(l[5:]).all()
+
+
+def test_full_size_draft_extend_sampled():
+    """The MTP-shaped batch with per-request lengths uniform in [1, 4], in the
+    launch configuration the benchmark times, on sampled rows."""
+    rg = ragged(generate("draft_extend"))
+    o, l = run_ragged(rg)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    rng = np.random.default_rng(9)
+    sel = [(int(rng.integers(rg.total_q)), int(rng.integers(128))) for _ in range(96)]
+    sel += [(int(rg.qo_indptr[b + 1]) - 1, 127) for b in range(0, rg.base.batch, 9)]
+    ro, rl = RG.decode_rows(oracle.default(), rg, sel)
+    G.compare(np.stack([o[t, h] for t, h in sel]), np.array([l[t, h] for t, h in sel]), ro, rl,
+              what="draft_extend")
