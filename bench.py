@@ -67,31 +67,39 @@ class HipEvents:
         self.hip.hipEventDestroy(ctypes.c_void_p(ev))
 
 
-def cpu_baseline(inp, budget_s: float = 10.0):
+def cpu_baseline(inp, budget_s: float = 10.0, rg=None):
     """The CPU oracle on the host cores over a bounded sample of the same workload:
     whole requests (all query rows) in batch order, cycling through the batch
     again if it is done early, until about budget_s seconds of oracle work (at
-    least one request)."""
+    least one request).  rg: the ragged packing of inp, if the workload has one."""
     import numpy as np
     import oracle
+    from oracle import ragged as oracle_ragged
     import paged_mla_decode_06_amd as mla
     orc = oracle.default()
     kv_bytes = 1 if inp.kv_fp8 else 2
     done, t_total = 0, 0.0
     while done == 0 or t_total < budget_s:
         b = done % inp.batch
-        sel = [(b, j, h) for j in range(inp.q_len) for h in range(inp.heads)]
         t0 = time.perf_counter()
-        orc.decode_rows(inp, sel)
+        if rg is None:
+            orc.decode_rows(inp, [(b, j, h) for j in range(inp.q_len) for h in range(inp.heads)])
+        else:
+            oracle_ragged.decode_rows(orc, rg, [(t, h) for t in range(int(rg.qo_indptr[b]), int(rg.qo_indptr[b + 1]))
+                                                for h in range(inp.heads)])
         t_total += time.perf_counter() - t0
         done += 1
-    lens = np.asarray(inp.seq_lens)[np.arange(done) % inp.batch]
-    nbytes, _ = mla.algorithmic_work(lens, inp.q_len, inp.heads, inp.page_size, kv_bytes)
+    idx = np.arange(done) % inp.batch
+    lens = np.asarray(inp.seq_lens)[idx]
+    if rg is None:
+        nbytes, _ = mla.algorithmic_work(lens, inp.q_len, inp.heads, inp.page_size, kv_bytes)
+    else:
+        nbytes, _ = mla.algorithmic_work_ragged(lens, rg.q_lens[idx], inp.heads, inp.page_size, kv_bytes)
     passes = f", {done / inp.batch:.2f} passes over the batch" if done > inp.batch else ""
     return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": orc.threads(), "kind": "oracle",
             "seconds": round(t_total, 3),
-            "sample": f"{done} whole requests in batch order{passes} (all {inp.q_len * inp.heads} query rows "
-                      f"each, {int(lens.sum())} cached tokens), fp64 C oracle, OpenMP over query rows; "
+            "sample": f"{done} whole requests in batch order{passes} (all their query rows, "
+                      f"{int(lens.sum())} cached tokens), fp64 C oracle, OpenMP over query rows; "
                       f"rate = the sample's algorithmic bytes / its time"}
 
 
@@ -135,9 +143,10 @@ def kernel_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per split-kernel launch from the committed counter summary of
-    this workload, or None when there is none or it was taken on other sources."""
+def measured_traffic(workload: str, whole_call: bool = False):
+    """HBM bytes per split-kernel launch (whole_call: split and combine kernels
+    together) from the committed counter summary of this workload, or None
+    when there is none or it was taken on other sources."""
     path = os.path.join(ROOT, "profiles", f"mla_split_kernel.{workload}.traffic.txt")
     if not os.path.exists(path):
         return None
@@ -150,7 +159,10 @@ def measured_traffic(workload: str):
     if fields.get("kernel_sources_sha256") != kernel_sources_sha256():
         return None
     try:
-        return int(fields["traffic_bytes_per_launch"])
+        t = int(fields["traffic_bytes_per_launch"])
+        if whole_call:
+            t += int(fields["combine_read_bytes_per_launch"]) + int(fields["combine_write_bytes_per_launch"])
+        return t
     except (KeyError, ValueError):
         return None
 
@@ -195,7 +207,7 @@ def main():
     import numpy as np
     import torch
     import paged_mla_decode_06_amd as mla
-    from mla_synth import generate, WORKLOADS
+    from mla_synth import generate, ragged, WORKLOADS
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -203,10 +215,17 @@ def main():
     w = WORKLOADS[args.workload]
     inp = generate(w)
     kv_bytes = 1 if inp.kv_fp8 else 2
-    nbytes, flops = mla.algorithmic_work(inp.seq_lens, inp.q_len, inp.heads, inp.page_size, kv_bytes)
+    # a ragged batch (per-request query lengths) runs through mla_decode_ragged
+    rg = ragged(inp) if w.ragged_q else None
+    q_lens = rg.q_lens if rg is not None else np.full(inp.batch, inp.q_len, dtype=np.int32)
+    if rg is not None:
+        nbytes, flops = mla.algorithmic_work_ragged(inp.seq_lens, q_lens, inp.heads, inp.page_size, kv_bytes)
+    else:
+        nbytes, flops = mla.algorithmic_work(inp.seq_lens, inp.q_len, inp.heads, inp.page_size, kv_bytes)
+    q_rows = int(q_lens.sum())    # query tokens of the step
 
     # device inputs, rotated over enough copies to exceed the last-level cache
-    q0 = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    q0 = torch.from_numpy((rg.q if rg is not None else inp.q).view(np.int16)).view(torch.bfloat16).to(dev)
     if inp.kv_fp8:
         pool0 = torch.from_numpy(inp.pool).view(torch.float8_e4m3fn).to(dev)
     else:
@@ -217,26 +236,40 @@ def main():
     pools = [pool0] + [pool0.clone() for _ in range(copies - 1)]
     bt = torch.from_numpy(inp.block_table).to(dev)
     sl = torch.from_numpy(inp.seq_lens).to(dev)
-    out = torch.empty((inp.batch, inp.q_len, inp.heads, 512), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((inp.batch, inp.q_len, inp.heads), dtype=torch.float32, device=dev)
-    p = mla.params_for(q0, pool0, bt, inp.max_seq_len, inp.softmax_scale, inp.k_scale,
-                       min_work_units=w.min_work_units)
+    out = torch.empty((q_rows, inp.heads, 512) if rg is not None else (inp.batch, inp.q_len, inp.heads, 512),
+                      dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(out.shape[:-1], dtype=torch.float32, device=dev)
+    p = mla.make_params(inp.batch, inp.q_len, inp.heads, inp.page_size, inp.num_pages, inp.block_table.shape[1],
+                        inp.max_seq_len, mla.MLA_KV_FP8_E4M3FN if inp.kv_fp8 else mla.MLA_KV_BF16,
+                        inp.softmax_scale, inp.k_scale, min_work_units=w.min_work_units)
     ws = mla.alloc_workspace(p, dev)
     stream = torch.cuda.current_stream()
+    ind = torch.from_numpy(rg.qo_indptr).to(dev) if rg is not None else None
 
     # Every timed step records an event before and after the split kernel on the
     # stream both kernels run on: the split kernel's duration is (start, end) of
-    # its own step, the GPU time of a whole step is (start, next start).
+    # its own step, the GPU time of a whole step is (start, next start).  A
+    # ragged call is bracketed as a whole (split kernel and combine).
     ev = HipEvents()
     events = [(ev.create(), ev.create()) for _ in range(args.steps)]
+
+    def step(i, e0, e1):
+        if rg is None:
+            mla.mla_decode_timed(p, qs[i % copies], pools[i % copies], bt, sl, out, lse, ws, stream, e0, e1, None)
+            return
+        if e0 is not None:
+            ev.record(e0, stream)
+        mla.mla_decode_ragged(qs[i % copies], ind, pools[i % copies], bt, sl, out, lse, ws, max_q_len=inp.q_len,
+                              max_seq_len=inp.max_seq_len, softmax_scale=inp.softmax_scale, stream=stream, params=p)
+        if e1 is not None:
+            ev.record(e1, stream)
+
     for i in range(args.warmup):
-        mla.mla_decode_timed(p, qs[i % copies], pools[i % copies], bt, sl, out, lse, ws, stream, None, None, None)
+        step(i, None, None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        i = args.warmup + k
-        mla.mla_decode_timed(p, qs[i % copies], pools[i % copies], bt, sl, out, lse, ws, stream,
-                             events[k][0], events[k][1], None)
+        step(args.warmup + k, events[k][0], events[k][1])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -255,7 +288,7 @@ def main():
     # longer uses.
     P = inp.page_size
     new_locs = [int(inp.block_table[b, t // P]) * P + t % P
-                for b in range(inp.batch) for t in range(max(int(inp.seq_lens[b]) - inp.q_len, 0),
+                for b in range(inp.batch) for t in range(max(int(inp.seq_lens[b]) - int(q_lens[b]), 0),
                                                         int(inp.seq_lens[b]))]
     step_rows = q0.view(-1, 576)[:len(new_locs)]
     step_locs = torch.tensor(new_locs, dtype=torch.int64, device=dev)
@@ -269,7 +302,7 @@ def main():
     kv_only = int(inp.seq_lens.astype(np.int64).sum()) * 576 * kv_bytes
     # the split kernel's own algorithmic bytes: everything but the output rows
     # and LSEs, which the combine kernel writes for split requests
-    split_bytes = nbytes - inp.batch * inp.q_len * inp.heads * (512 * 2 + 4)
+    split_bytes = nbytes - q_rows * inp.heads * (512 * 2 + 4) if rg is None else nbytes
     split_gbs = split_bytes / (split_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -284,27 +317,30 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8_e4m3fn-kv/bf16" if inp.kv_fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": inp.batch, "q_len": inp.q_len, "heads": inp.heads,
+        "config": {"workload": w.name, "batch": inp.batch,
+                   "q_len": f"ragged 1..{inp.q_len}" if rg is not None else inp.q_len, "query_tokens": q_rows,
+                   "heads": inp.heads,
                    "page_size": inp.page_size, "kv_dtype": w.kv, "seq_lens": f"{w.lens}", "seed": w.seed,
                    "cached_tokens": int(inp.seq_lens.sum()), "num_pages": inp.num_pages,
                    "rotating_copies": copies},
         "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "kv_gbs": round(kv_only / (ms_step * 1e-3) / 1e9, 2),
-        "decode_tokens_per_s": round(inp.batch * inp.q_len / (ms_step * 1e-3), 1),
+        "decode_tokens_per_s": round(q_rows / (ms_step * 1e-3), 1),
         "algorithmic_bytes": nbytes,
         "algorithmic_flops": flops,
         "event_ms": {"split_kernel": round(split_ms, 5), "gpu_step": round(gpu_step_ms, 5),
                      "combine_and_launch_gaps": round(gpu_step_ms - split_ms, 5)},
         "roofline": {"bound": "hbm", "achieved": round(split_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "mla_split_kernel", "algorithmic_bytes_per_launch": split_bytes,
+                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, whole_call=rg is not None),
+                     "kernel": "mla_split_kernel" if rg is None else "mla_split_kernel + mla_combine_kernel (one call)",
+                     "algorithmic_bytes_per_launch": split_bytes,
                      "mfma_frac": round(flops / (split_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
         "path_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
         "kv_append": append_step,
         "kv_append_32k_rows": append_big,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s, rg)
     print(json.dumps(res))
 
 
