@@ -62,6 +62,9 @@ constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
 #ifndef MLA_F8_SC
 #define MLA_F8_SC 4
 #endif
+#ifndef MLA_F8_DEFER
+#define MLA_F8_DEFER 1
+#endif
 constexpr int kRowsPerWave = 16 * kRowBlocksPerWave;
 static_assert(kRowBlocksPerWave == 1, "one 16-row MFMA block per wave");
 // A split workgroup runs three kinds of wave in a pipeline over the KV tiles
@@ -677,20 +680,47 @@ __device__ void load_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, c
   const int nt = pc.tile1 - pc.tile0;
   PageWindow pw;
   pw.init(a, b, (pc.tile0 * kTile) / a.P, (tok_end + a.P - 1) / a.P);
-  auto put = [&](int t) {   // tile t of the piece into its ring buffer
-    if constexpr (FP8) {
+  if constexpr (FP8) {
+#if MLA_F8_DEFER
+    // fp8 codes go through registers: tile t's codes are loaded in interval
+    // t-3 and converted into LDS in interval t-2 (its buffer is free from
+    // then on), so each tile's HBM latency overlaps a whole interval instead
+    // of stalling the loader wave in the interval that issues it.
+    auto load = [&](int t) { stg.load(a, pw, b, (pc.tile0 + t) * kTile, tok_end); };
+    auto store = [&](int t) { stg.store(lds + tile_buf(t) * kTileBytes); };   // waits for tile t's loads
+    if (nt > 0) {
+      load(0);
+      store(0);
+    }
+    if (nt > 1) load(1);
+    for (int j = -1; j < nt; j++) {
+      // tile j+1 is in LDS before barrier j
+      lds_barrier();
+      if (j + 2 < nt) store(j + 2);
+      if (j + 3 < nt) load(j + 3);
+    }
+#else
+    auto put = [&](int t) {
       stg.load(a, pw, b, (pc.tile0 + t) * kTile, tok_end);
       stg.store(lds + tile_buf(t) * kTileBytes);   // waits for its own loads
-    } else {
-      stg.issue(a, lds + tile_buf(t) * kTileBytes, pw, b, (pc.tile0 + t) * kTile, tok_end, lw);
+    };
+    for (int t = 0; t < 2 && t < nt; t++) put(t);
+    for (int j = -1; j < nt; j++) {
+      lds_barrier();
+      if (j + 3 < nt) put(j + 3);
     }
-  };
-  for (int t = 0; t < 2 && t < nt; t++) put(t);
-  for (int j = -1; j < nt; j++) {
-    // tile j+1 is in LDS before barrier j; tile j+2 may still be in flight
-    if constexpr (!FP8) stg.wait(j + 2 < nt ? 1 : 0);
-    lds_barrier();
-    if (j + 3 < nt) put(j + 3);
+#endif
+  } else {
+    auto put = [&](int t) {   // tile t of the piece into its ring buffer
+      stg.issue(a, lds + tile_buf(t) * kTileBytes, pw, b, (pc.tile0 + t) * kTile, tok_end, lw);
+    };
+    for (int t = 0; t < 2 && t < nt; t++) put(t);
+    for (int j = -1; j < nt; j++) {
+      // tile j+1 is in LDS before barrier j; tile j+2 may still be in flight
+      stg.wait(j + 2 < nt ? 1 : 0);
+      lds_barrier();
+      if (j + 3 < nt) put(j + 3);
+    }
   }
   lds_barrier();
   lds_barrier();
