@@ -214,6 +214,22 @@ def ragged(inp: Inputs, q_lens: Optional[np.ndarray] = None, seed: Optional[int]
     return Ragged(inp, np.ascontiguousarray(q.reshape(-1, H, D)), indptr, q_lens)
 
 
+def rope_cache(max_position: int, base: float = 10000.0, dim: int = ROPE_DIM) -> np.ndarray:
+    """A rotary-embedding cos/sin cache [max_position, dim] float32: row p holds
+    cos(p * f_i) in columns 0..dim/2-1 and sin(p * f_i) after them, with the
+    frequencies f_i = base^(-2i/dim) of the original rotary embedding."""
+    inv = base ** (-np.arange(0, dim, 2, dtype=np.float64) / dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def decode_positions(inp: Inputs) -> np.ndarray:
+    """Positions [B, q_len] of each request's new query tokens: L_b - q_len + j
+    (the cached tokens count the new ones)."""
+    L = np.asarray(inp.seq_lens, dtype=np.int64)
+    return np.maximum(L[:, None] - inp.q_len + np.arange(inp.q_len)[None, :], 0)
+
+
 def poison_unused(inp: Inputs) -> None:
     """Write NaN into every pool slot that no request's visible tokens cover."""
     nan = FP8_NAN if inp.kv_fp8 else BF16_NAN

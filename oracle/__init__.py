@@ -9,6 +9,8 @@ Two independent implementations live here:
   OpenMP over query rows.  This is what GPU results are compared with.
 * ``brute.py``: dense numpy fp64 attention over the gathered rows, used to
   pin the C oracle on small inputs.
+* ``rope.py``: the rotary embedding of the query and key rope parts, pinned by
+  ``tests/test_oracle_rope.py``.
 * ``kv_append.py``: the KV-cache append (scatter of new latent rows into the
   pool, with the e4m3fn quantisation of an fp8 pool), pinned by
   ``tests/test_oracle_append.py``.
