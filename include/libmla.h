@@ -171,6 +171,34 @@ mla_status mla_decode_ragged(const mla_decode_params* p, const void* q, const in
 mla_status mla_check_qo_indptr_host(const mla_decode_params* p, const int32_t* qo_indptr_host,
                                     int32_t total_q_tokens);
 
+/* Rotary embedding of the 64-wide rope parts, the one the pages hand to
+ * their rope kernel with the token positions (forward_decode of
+ * TRTLLMMLABackend on "sglang trtllm_mla_backend.py": forward_batch.positions,
+ * cos_sin_cache and is_neox).  Token t's rope part is turned pair by pair:
+ * pair i = (x1, x2) is (dim i, dim i+32) when is_neox, else (dim 2i, dim
+ * 2i+1), and becomes (x1 c - x2 s, x2 c + x1 s) with c, s = columns i and
+ * 32+i of cache row clamp(positions[t], 0, max_position-1).  Each product and
+ * the difference or sum is an fp32 operation (no fused multiply-add), and the
+ * result is rounded to bf16 (nearest even). */
+typedef struct {
+  const int64_t* positions;     /* device, int64 [tokens], 8-byte aligned */
+  const float* cos_sin_cache;   /* device, fp32 [max_position][64]: cos in 0..31, sin in 32..63; 16-byte aligned */
+  int32_t max_position;         /* rows of the cache, >= 1 */
+  int32_t is_neox;              /* 1: pairs (i, i+32); 0: pairs (2i, 2i+1) */
+} mla_rope;
+
+/* mla_decode_qparts() that first turns every query row's rope part by the
+ * rotary embedding at its token's position (token = b * q_len + j indexes
+ * rope->positions): the rotation the pages apply to q_rope before the decode
+ * kernel, done here on the fragments in registers, so the rotated query is
+ * never written out.  Errors as mla_decode_qparts(); an invalid rope
+ * description (null pointers, max_position < 1, is_neox not 0 or 1, a
+ * misaligned cache or positions array) is MLA_ERR_INVALID_VALUE. */
+mla_status mla_decode_qparts_rope(const mla_decode_params* p, const void* q_nope, const void* q_rope,
+                                  const mla_query_layout* layout, const mla_rope* rope, const void* kv_pool,
+                                  const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* mla_decode() that also records three caller-created HIP events (hipEvent_t,
  * each may be NULL) on `stream`: before the split-KV kernel, between it and
  * the combine kernel, and after the combine, so that a benchmark can time the
@@ -251,6 +279,14 @@ typedef struct {
  * errors (MLA_ERR_INVALID_VALUE / MLA_ERR_NOT_SUPPORTED) enqueue nothing. */
 mla_status mla_kv_append(const mla_kv_append_params* p, const void* k_nope, const void* k_rope,
                          const int64_t* out_cache_loc, void* kv_pool, void* stream);
+
+/* mla_kv_append() that turns each new row's rope part by the rotary
+ * embedding at its position (rope->positions indexed by row i) before it is
+ * stored: the key half of the pages' rope-then-write sequence (the rotated
+ * rope part is rounded to bf16 first, then stored or quantised as by
+ * mla_kv_append()).  Errors as mla_kv_append() and mla_decode_qparts_rope(). */
+mla_status mla_kv_append_rope(const mla_kv_append_params* p, const void* k_nope, const void* k_rope,
+                              const int64_t* out_cache_loc, const mla_rope* rope, void* kv_pool, void* stream);
 
 #ifdef __cplusplus
 }

@@ -54,6 +54,11 @@ class mla_query_layout(ctypes.Structure):
                                              "rope_head_stride")]
 
 
+class mla_rope(ctypes.Structure):
+    _fields_ = [("positions", ctypes.c_void_p), ("cos_sin_cache", ctypes.c_void_p), ("max_position", ctypes.c_int32),
+                ("is_neox", ctypes.c_int32)]
+
+
 class mla_kv_append_params(ctypes.Structure):
     _fields_ = [("nope_stride", ctypes.c_int64), ("rope_stride", ctypes.c_int64)] + [
         (n, ctypes.c_int32) for n in ("num_tokens", "kv_lora_rank", "qk_rope_head_dim", "page_size", "num_pages",
@@ -98,6 +103,12 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_ragged.argtypes = [P, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.mla_check_qo_indptr_host.restype = ctypes.c_int
         L.mla_check_qo_indptr_host.argtypes = [P, vp, ctypes.c_int32]
+        L.mla_decode_qparts_rope.restype = ctypes.c_int
+        L.mla_decode_qparts_rope.argtypes = [P, vp, vp, ctypes.POINTER(mla_query_layout), ctypes.POINTER(mla_rope),
+                                             vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.mla_kv_append_rope.restype = ctypes.c_int
+        L.mla_kv_append_rope.argtypes = [ctypes.POINTER(mla_kv_append_params), vp, vp, vp, ctypes.POINTER(mla_rope),
+                                         vp, vp]
         L.mla_kv_append.restype = ctypes.c_int
         L.mla_kv_append.argtypes = [ctypes.POINTER(mla_kv_append_params), vp, vp, vp, vp, vp]
         _lib = L
@@ -226,13 +237,29 @@ def _token_head_strides(t, B: int, q_len: int, H: int, width: int, name: str):
     raise ValueError(f"{name}: expected [B, q_len, H, {width}] or [B*q_len, H, {width}]")
 
 
+def _rope_struct(positions, cos_sin_cache, is_neox: bool):
+    """mla_rope for GPU tensors positions (int64 [tokens]) and cos_sin_cache
+    (float32 [max_position, 64], contiguous)."""
+    import torch
+    if positions.dtype != torch.int64 or not positions.is_contiguous() or not positions.is_cuda:
+        raise ValueError("positions must be a contiguous int64 GPU tensor")
+    if (cos_sin_cache.dtype != torch.float32 or not cos_sin_cache.is_contiguous() or not cos_sin_cache.is_cuda
+            or cos_sin_cache.dim() != 2 or cos_sin_cache.shape[1] != 64):
+        raise ValueError("cos_sin_cache must be a contiguous float32 [max_position, 64] GPU tensor")
+    return mla_rope(int(positions.data_ptr()), int(cos_sin_cache.data_ptr()), int(cos_sin_cache.shape[0]),
+                    1 if is_neox else 0)
+
+
 def mla_decode_qparts(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse=None, workspace=None, *,
                       max_seq_len: int, softmax_scale: float, k_scale: float = 1.0, num_splits: int = 0,
-                      min_work_units: int = 0, stream=None):
+                      min_work_units: int = 0, stream=None, positions=None, cos_sin_cache=None,
+                      is_neox: bool = True):
     """mla_decode with the query as its latent part q_nope (512 wide) and rope
     part q_rope (64 wide), each [B, q_len, H, w] or [B*q_len, H, w] with any
     token and head strides (multiples of 8 elements): read in place, no
-    concatenation.  out [B, q_len, H, 512] fixes B, q_len and H."""
+    concatenation.  out [B, q_len, H, 512] fixes B, q_len and H.  With
+    positions (int64 [B*q_len]) and cos_sin_cache (float32 [max_pos, 64]) the
+    rope part is first turned by the rotary embedding (mla_decode_qparts_rope)."""
     import torch
     for name, t in (("q_nope", q_nope), ("q_rope", q_rope), ("kv_pool", kv_pool), ("block_table", block_table),
                     ("seq_lens", seq_lens), ("out", out)):
@@ -258,9 +285,18 @@ def mla_decode_qparts(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse=N
     if workspace is None:
         workspace = alloc_workspace(p, out.device)
     lay = mla_query_layout(int(nt), int(nh), int(rt), int(rh))
+    wsb = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    if cos_sin_cache is not None:
+        if positions is None or positions.numel() != B * ql:
+            raise ValueError("positions must hold one position per query token (B * q_len)")
+        r = _rope_struct(positions, cos_sin_cache, is_neox)
+        st = lib().mla_decode_qparts_rope(ctypes.byref(p), _ptr(q_nope), _ptr(q_rope), ctypes.byref(lay),
+                                          ctypes.byref(r), _ptr(kv_pool), _ptr(block_table), _ptr(seq_lens),
+                                          _ptr(out), _ptr(lse), _ptr(workspace), wsb, _stream_handle(stream))
+        _check(st, "mla_decode_qparts_rope")
+        return out, lse
     st = lib().mla_decode_qparts(ctypes.byref(p), _ptr(q_nope), _ptr(q_rope), ctypes.byref(lay), _ptr(kv_pool),
-                                 _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace),
-                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                 _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace), wsb,
                                  _stream_handle(stream))
     _check(st, "mla_decode_qparts")
     return out, lse
@@ -376,7 +412,8 @@ def make_append_params(num_tokens: int, page_size: int, num_pages: int, kv_dtype
 
 
 def mla_kv_append(k_nope, k_rope, out_cache_loc, kv_pool, *, k_scale: float = 1.0, stream=None,
-                  params: Optional[mla_kv_append_params] = None):
+                  params: Optional[mla_kv_append_params] = None, positions=None, cos_sin_cache=None,
+                  is_neox: bool = True):
     """Enqueue the cache write of T new rows on ``stream`` (default: torch's current stream).
 
     k_nope [T, 512] and k_rope [T, 64] bf16 (rows may be strided, e.g. the two
@@ -405,6 +442,13 @@ def mla_kv_append(k_nope, k_rope, out_cache_loc, kv_pool, *, k_scale: float = 1.
     p = params if params is not None else make_append_params(
         T, P, N, MLA_KV_FP8_E4M3FN if fp8 else MLA_KV_BF16, k_scale,
         k_nope.stride(0) if T > 1 else LATENT_DIM, k_rope.stride(0) if T > 1 else ROPE_DIM)
+    if cos_sin_cache is not None:
+        if positions is None or positions.numel() != T:
+            raise ValueError("positions must hold one position per row")
+        r = _rope_struct(positions, cos_sin_cache, is_neox)
+        _check(lib().mla_kv_append_rope(ctypes.byref(p), _ptr(k_nope), _ptr(k_rope), _ptr(out_cache_loc),
+                                        ctypes.byref(r), _ptr(kv_pool), _stream_handle(stream)), "mla_kv_append_rope")
+        return kv_pool
     _check(lib().mla_kv_append(ctypes.byref(p), _ptr(k_nope), _ptr(k_rope), _ptr(out_cache_loc), _ptr(kv_pool),
                                _stream_handle(stream)), "mla_kv_append")
     return kv_pool

@@ -129,7 +129,16 @@ struct QueryParts {
   mla_query_layout s;
   const int32_t* qo_indptr = nullptr;   // ragged batch: per-request query token offsets [B+1]
   int32_t total_q = 0;                  // ragged batch: query tokens in q and out
+  const mla_rope* rotary = nullptr;     // rotary embedding of the rope part, or none
 };
+
+// Host checks of a rotary-embedding description.
+mla_status check_rope(const mla_rope* r) {
+  if (r == nullptr || r->positions == nullptr || r->cos_sin_cache == nullptr) return MLA_ERR_INVALID_VALUE;
+  if (r->max_position < 1 || (r->is_neox != 0 && r->is_neox != 1)) return MLA_ERR_INVALID_VALUE;
+  if (((uintptr_t)r->cos_sin_cache & 15) != 0 || ((uintptr_t)r->positions & 7) != 0) return MLA_ERR_INVALID_VALUE;
+  return MLA_OK;
+}
 
 QueryParts merged_query(const mla_decode_params* p, const void* q) {
   QueryParts qp;
@@ -209,6 +218,10 @@ static mla_status decode_impl(const mla_decode_params* p, const QueryParts& qp, 
   a.qr_tok = qp.s.rope_token_stride;
   a.qr_head = qp.s.rope_head_stride;
   a.qo_indptr = qp.qo_indptr;
+  a.positions = qp.rotary != nullptr ? qp.rotary->positions : nullptr;
+  a.rope_cs = qp.rotary != nullptr ? qp.rotary->cos_sin_cache : nullptr;
+  a.rope_max_pos = qp.rotary != nullptr ? qp.rotary->max_position : 0;
+  a.rope_neox = qp.rotary != nullptr ? qp.rotary->is_neox : 0;
   a.total_q = qp.qo_indptr != nullptr ? qp.total_q : p->batch * p->q_len;
   a.pool = kv_pool;
   a.bt = block_table;
@@ -297,6 +310,22 @@ mla_status mla_check_qo_indptr_host(const mla_decode_params* p, const int32_t* q
   }
   if (p->batch > 0 && qo_indptr_host[p->batch] != total_q_tokens) return MLA_ERR_INVALID_VALUE;
   return MLA_OK;
+}
+
+mla_status mla_decode_qparts_rope(const mla_decode_params* p, const void* q_nope, const void* q_rope,
+                                  const mla_query_layout* layout, const mla_rope* rope, const void* kv_pool,
+                                  const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (layout == nullptr) return MLA_ERR_INVALID_VALUE;
+  mla_status s = check_rope(rope);
+  if (s != MLA_OK) return s;
+  QueryParts qp;
+  qp.nope = q_nope;
+  qp.rope = q_rope;
+  qp.s = *layout;
+  qp.rotary = rope;
+  return decode_impl(p, qp, kv_pool, block_table, seq_lens, out, lse, workspace, workspace_bytes, stream, nullptr,
+                     nullptr, nullptr);
 }
 
 mla_status mla_decode_qparts(const mla_decode_params* p, const void* q_nope, const void* q_rope,
@@ -414,8 +443,8 @@ mla_status mla_plan_device(const mla_decode_params* p, const int32_t* seq_lens, 
   return MLA_OK;
 }
 
-mla_status mla_kv_append(const mla_kv_append_params* p, const void* k_nope, const void* k_rope,
-                         const int64_t* out_cache_loc, void* kv_pool, void* stream) {
+static mla_status kv_append_impl(const mla_kv_append_params* p, const void* k_nope, const void* k_rope,
+                                 const int64_t* out_cache_loc, const mla_rope* rope, void* kv_pool, void* stream) {
   if (p == nullptr) return MLA_ERR_INVALID_VALUE;
   if (p->kv_lora_rank != mla::kLatentDim || p->qk_rope_head_dim != mla::kRowDim - mla::kLatentDim)
     return MLA_ERR_NOT_SUPPORTED;
@@ -446,8 +475,24 @@ mla_status mla_kv_append(const mla_kv_append_params* p, const void* k_nope, cons
   a.T = p->num_tokens;
   a.fp8 = p->kv_dtype == MLA_KV_FP8_E4M3FN ? 1 : 0;
   a.k_scale = a.fp8 ? p->k_scale : 1.f;
+  a.positions = rope != nullptr ? rope->positions : nullptr;
+  a.rope_cs = rope != nullptr ? rope->cos_sin_cache : nullptr;
+  a.rope_max_pos = rope != nullptr ? rope->max_position : 0;
+  a.rope_neox = rope != nullptr ? rope->is_neox : 0;
   if (mla_launch_append(&a, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
+}
+
+mla_status mla_kv_append(const mla_kv_append_params* p, const void* k_nope, const void* k_rope,
+                         const int64_t* out_cache_loc, void* kv_pool, void* stream) {
+  return kv_append_impl(p, k_nope, k_rope, out_cache_loc, nullptr, kv_pool, stream);
+}
+
+mla_status mla_kv_append_rope(const mla_kv_append_params* p, const void* k_nope, const void* k_rope,
+                              const int64_t* out_cache_loc, const mla_rope* rope, void* kv_pool, void* stream) {
+  mla_status s = check_rope(rope);
+  if (s != MLA_OK) return s;
+  return kv_append_impl(p, k_nope, k_rope, out_cache_loc, rope, kv_pool, stream);
 }
 
 mla_status mla_check_inputs_host(const mla_decode_params* p, const int32_t* block_table_host,

@@ -8,7 +8,9 @@
 // takes the bits unchanged; an fp8 pool takes the OCP e4m3fn code of
 // x / k_scale (fp32 quotient, saturated to +-448, round to nearest even; NaN
 // stores 0x7F), the per-tensor scale convention of scaled_fp8_quant in
-// _quantize_fp8_qkv on "sglang trtllm_mla_backend.py".
+// _quantize_fp8_qkv on "sglang trtllm_mla_backend.py".  With a rotary
+// embedding (mla_kv_append_rope) the rope part is first turned at the row's
+// position (mla_rope.h) and rounded to bf16, then stored or quantised.
 //
 // HBM-bound and embarrassingly parallel: one thread per 16-byte input chunk
 // (8 bf16 elements), 72 chunks per row, consecutive threads on consecutive
@@ -18,6 +20,7 @@
 #include <stdint.h>
 
 #include "mla_args.h"
+#include "mla_rope.h"
 
 namespace mla {
 
@@ -64,18 +67,35 @@ __global__ __launch_bounds__(kAppendThreads) void mla_append_kernel(AppendArgs a
     if ((uint64_t)loc >= (uint64_t)a.slots) continue;   // out-of-range slots are skipped
     const uint16_t* src = c < kAppendNopeChunks ? a.nope + i * a.nope_stride + 8 * c
                                                 : a.rope + i * a.rope_stride + 8 * (c - kAppendNopeChunks);
-    const app_u32x4_t x = *(const app_u32x4_t*)src;
-    if (!a.fp8) {
-      *(app_u32x4_t*)((uint16_t*)a.pool + loc * 576 + 8 * c) = x;
-    } else {
-      const float s = a.k_scale;
-      app_u32x2_t y;
-      y[0] = e4m3fn_x4(scaled(bf16_lo(x[0]), s), scaled(bf16_hi(x[0]), s), scaled(bf16_lo(x[1]), s),
-                       scaled(bf16_hi(x[1]), s));
-      y[1] = e4m3fn_x4(scaled(bf16_lo(x[2]), s), scaled(bf16_hi(x[2]), s), scaled(bf16_lo(x[3]), s),
-                       scaled(bf16_hi(x[3]), s));
-      *(app_u32x2_t*)((uint8_t*)a.pool + loc * 576 + 8 * c) = y;
+    app_u32x4_t x = *(const app_u32x4_t*)src;
+    auto put = [&](int cc, app_u32x4_t v) {
+      if (!a.fp8) {
+        *(app_u32x4_t*)((uint16_t*)a.pool + loc * 576 + 8 * cc) = v;
+      } else {
+        const float s = a.k_scale;
+        app_u32x2_t y;
+        y[0] = e4m3fn_x4(scaled(bf16_lo(v[0]), s), scaled(bf16_hi(v[0]), s), scaled(bf16_lo(v[1]), s),
+                         scaled(bf16_hi(v[1]), s));
+        y[1] = e4m3fn_x4(scaled(bf16_lo(v[2]), s), scaled(bf16_hi(v[2]), s), scaled(bf16_lo(v[3]), s),
+                         scaled(bf16_hi(v[3]), s));
+        *(app_u32x2_t*)((uint8_t*)a.pool + loc * 576 + 8 * cc) = y;
+      }
+    };
+    if (a.rope_cs != nullptr && c >= kAppendNopeChunks) {
+      // rotary embedding of the key's rope part before it is stored: chunk
+      // q holds rope dims 8q..8q+7
+      const int q = c - kAppendNopeChunks;
+      const float* cs = rope_row(a.rope_cs, a.positions, i, a.rope_max_pos);
+      if (a.rope_neox) {
+        if (q >= 4) continue;   // rotated and stored with its partner chunk q - 4
+        app_u32x4_t x2 = *(const app_u32x4_t*)(src + 32);
+        rope_rotate_halves(x, x2, cs, 8 * q);
+        put(c + 4, x2);
+      } else {
+        rope_rotate_interleaved(x, cs, 8 * q);
+      }
     }
+    put(c, x);
   }
 }
 

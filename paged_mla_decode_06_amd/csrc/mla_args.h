@@ -19,6 +19,11 @@ struct SplitArgs {
   int32_t* pos_off_ws;      // [B+1] cost-position offsets (balanced mode), written by workgroup 0
   const int32_t* qo_indptr;  // ragged batch: request b's query tokens are [qo_indptr[b], qo_indptr[b+1]); null: b*q_len + j
   int32_t total_q;          // ragged batch: query tokens in q / out (bounds the offsets)
+  // rotary embedding of the query's rope part (null rope_cs: none): token t
+  // is turned by row clamp(positions[t], 0, rope_max_pos-1) of rope_cs
+  const int64_t* positions;
+  const float* rope_cs;     // [rope_max_pos][64] fp32: cos 0..31, sin 32..63
+  int32_t rope_max_pos, rope_neox;
   int32_t B, q_len, H, P, W, N, max_seq_len, nrb, R, num_splits;
   int64_t NG;   // groups of the plan
   float scale_log2;         // softmax_scale * (k_scale for fp8) * log2(e)
@@ -48,6 +53,10 @@ struct AppendArgs {
   int32_t T;
   int32_t fp8;
   float k_scale;            // fp8: stored code = e4m3fn(x / k_scale)
+  // rotary embedding of the rope part before it is stored (null rope_cs: none)
+  const int64_t* positions;
+  const float* rope_cs;
+  int32_t rope_max_pos, rope_neox;
 };
 
 }  // namespace mla

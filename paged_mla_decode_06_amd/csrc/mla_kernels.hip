@@ -26,6 +26,7 @@
 
 #include "mla_args.h"
 #include "mla_plan.h"
+#include "mla_rope.h"
 
 namespace mla {
 
@@ -758,6 +759,17 @@ __device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
     const int64_t h = row_ok ? hrow : 0;
     u32x4_t qv[kQSteps];
     load_q_fragments(qv, a.q + tok * a.qn_tok + h * a.qn_head + 8 * g, a.q_rope + tok * a.qr_tok + h * a.qr_head + 8 * g);
+    if (a.rope_cs != nullptr && row_ok) {
+      // rotary embedding of the rope part at the token's position: lane g
+      // holds rope dims 8g..8g+7 (fragment 16) and 32+8g..32+8g+7 (17)
+      const float* cs = rope_row(a.rope_cs, a.positions, tok, a.rope_max_pos);
+      if (a.rope_neox) {
+        rope_rotate_halves(qv[16], qv[17], cs, 8 * g);
+      } else {
+        rope_rotate_interleaved(qv[16], cs, 8 * g);
+        rope_rotate_interleaved(qv[17], cs, 32 + 8 * g);
+      }
+    }
 #pragma unroll
     for (int k = 0; k < kQSteps; k++) qf[k] = __builtin_bit_cast(bf16x8_t, row_ok ? qv[k] : u32x4_t{0u, 0u, 0u, 0u});
   }

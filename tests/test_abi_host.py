@@ -272,3 +272,29 @@ def test_ragged_algorithmic_work():
     nu, fu = mla.algorithmic_work(np.array([10]), 1, 2, 32, 2)
     assert fl == 2 * 2 * 1088 * (10 + 18 + 19 + 20)
     assert nb == 30 * 1152 + 4 * 2 * (1152 + 1024 + 4) + 4 * 2 + 8 + 12
+
+
+# ---- rotary embedding: argument checks before any device call
+@pytest.mark.parametrize("rope,ok", [
+    ((0x100000, 0x200000, 4096, 1), True),
+    ((0x100000, 0x200000, 4096, 0), True),
+    ((0, 0x200000, 4096, 1), False),            # no positions
+    ((0x100000, 0, 4096, 1), False),            # no cache
+    ((0x100000, 0x200000, 0, 1), False),        # empty cache
+    ((0x100000, 0x200000, 64, 2), False),       # is_neox must be 0 or 1
+    ((0x100000, 0x200008, 64, 1), False),       # cache not 16-byte aligned
+    ((0x100004, 0x200000, 64, 1), False),       # positions not 8-byte aligned
+])
+def test_rope_checks(L, rope, ok):
+    r = mla.mla_rope(*rope)
+    p = good()
+    lay = mla.mla_query_layout(576 * 16, 576, 576 * 16, 576)
+    fake = ctypes.c_void_p(0x100000)
+    st = L.mla_decode_qparts_rope(ctypes.byref(p), fake, ctypes.c_void_p(0x300000), ctypes.byref(lay),
+                                  ctypes.byref(r), fake, fake, fake, fake, None, ctypes.c_void_p(0x200000), 1, None)
+    assert st == (mla.MLA_ERR_WORKSPACE_TOO_SMALL if ok else mla.MLA_ERR_INVALID_VALUE)
+    pa = good_append(kv_dtype=mla.MLA_KV_FP8_E4M3FN, k_scale=0.0)   # invalid append params
+    st = L.mla_kv_append_rope(ctypes.byref(pa), fake, fake, fake, ctypes.byref(r), fake, None)
+    assert st == mla.MLA_ERR_INVALID_VALUE
+    assert L.mla_kv_append_rope(ctypes.byref(good_append()), fake, fake, fake, None, fake, None) == \
+        mla.MLA_ERR_INVALID_VALUE
