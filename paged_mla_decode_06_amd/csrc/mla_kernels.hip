@@ -1063,17 +1063,29 @@ __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a
 }
 
 // ---- combine: merge the partial results of each split row block by LSE
-// One wave per query row: lanes load the pieces' LSEs in parallel, then the
-// 512-wide bf16 partials are summed with weights exp(lse_s - LSE).
-constexpr int kCombineRowsPerBlock = kThreads / 64;
+// Lanes load the pieces' LSEs in parallel, then the 512-wide bf16 partials
+// are summed with weights exp(lse_s - LSE).  kWaves = 1: one wave per query
+// row, four rows per workgroup (few pieces per row).  kWaves = 4: the four
+// waves of a workgroup share one row, each summing every fourth group of
+// eight pieces, and add up through LDS -- four times the loads in flight per
+// row when rows have many pieces (long requests split over many workgroups).
+template <int kWaves>
+struct CombineShape {
+  static constexpr int kRowsPerWg = kWaves == 1 ? kThreads / 64 : 1;
+};
 
-// At most 64 VGPRs: eight workgroups per CU, so the grid of a full-size decode
-// (up to 2048 workgroups) runs in one round.
-__global__ __launch_bounds__(kThreads, 8) void mla_combine_kernel(CombineArgs a) {
+// One row per wave: at most 64 VGPRs, eight workgroups per CU, so the grid of
+// a full-size decode (up to 2048 workgroups) runs in one round.  One row per
+// workgroup: fewer, wider workgroups, up to 128 VGPRs.
+template <int kWaves>
+__global__ __launch_bounds__(kThreads, kWaves == 1 ? 8 : 4) void mla_combine_kernel(CombineArgs a) {
+  static_assert(kWaves == 1 || kWaves == kThreads / 64, "one wave per row, or the whole workgroup");
+  constexpr int kRowsPerWg = CombineShape<kWaves>::kRowsPerWg;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int chunks = kRowsPerBlock / kCombineRowsPerBlock;
+  const int ws = kWaves == 1 ? 0 : wave;       // this wave's share of the pieces
+  const int chunks = kRowsPerBlock / kRowsPerWg;
   const int64_t blk = blockIdx.x / chunks;     // b * nrb + rb
-  const int row_in_blk = (int)(blockIdx.x - blk * chunks) * kCombineRowsPerBlock + wave;
+  const int row_in_blk = (int)(blockIdx.x - blk * chunks) * kRowsPerWg + (kWaves == 1 ? wave : 0);
   const int32_t b = (int32_t)(blk / a.nrb), rb = (int32_t)(blk - (int64_t)b * a.nrb);
   const int row = rb * kRowsPerBlock + row_in_blk;
   const QExtent qe = q_extent<true>(a, b);
@@ -1135,7 +1147,7 @@ __global__ __launch_bounds__(kThreads, 8) void mla_combine_kernel(CombineArgs a)
     const int32_t s32 = s >= 0 ? (int32_t)s : 0;
     const float ls = s >= 0 ? a.part_lse[s * kRowsPerBlock + row_in_blk] : kNegInf;
     u32x4_t v[8];
-    load8(s32, 0, v);
+    load8(s32, 8 * ws, v);
     M = ls;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
@@ -1143,8 +1155,8 @@ __global__ __launch_bounds__(kThreads, 8) void mla_combine_kernel(CombineArgs a)
       const float w = ls == kNegInf ? 0.f : __expf(ls - M);
       den = w;
       const int cnt = (int)n;
-      accum8(w, 0, cnt, v);
-      for (int j = 8; j < cnt; j += 8) {
+      if (8 * ws < cnt) accum8(w, 8 * ws, cnt, v);
+      for (int j = 8 * ws + 8 * kWaves; j < cnt; j += 8 * kWaves) {
         load8(s32, j, v);
         accum8(w, j, cnt, v);
       }
@@ -1167,7 +1179,7 @@ __global__ __launch_bounds__(kThreads, 8) void mla_combine_kernel(CombineArgs a)
         const float w = ls == kNegInf ? 0.f : __expf(ls - M);
         den += w;
         const int cnt = (int)min((int64_t)64, n - c0);
-        for (int j = 0; j < cnt; j += 8) {
+        for (int j = 8 * ws; j < cnt; j += 8 * kWaves) {
           u32x4_t v[8];
           load8(s32, j, v);
           accum8(w, j, cnt, v);
@@ -1177,6 +1189,20 @@ __global__ __launch_bounds__(kThreads, 8) void mla_combine_kernel(CombineArgs a)
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) den += __shfl_xor(den, d);
+  if constexpr (kWaves > 1) {
+    // every wave holds the full denominator; wave 0 adds the others' sums
+    __shared__ float red[kWaves - 1][kLatentDim];
+    if (wave > 0) {
+#pragma unroll
+      for (int e = 0; e < 8; e++) red[wave - 1][8 * lane + e] = o[e];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int r = 0; r < kWaves - 1; r++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) o[e] += red[r][8 * lane + e];
+  }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int32_t jq = row / a.H, h = row - jq * a.H;
   const int64_t orow = (qe.tok0 + jq) * a.H + h;
@@ -1277,9 +1303,15 @@ hipError_t mla_launch_split(const mla::SplitArgs* a, int fp8, hipStream_t stream
 }
 
 hipError_t mla_launch_combine(const mla::CombineArgs* a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a->B * a->nrb * (mla::kRowsPerBlock / mla::kCombineRowsPerBlock);
+  // a workgroup per row when requests are split into many pieces on average
+  const bool wide = a->num_splits > 0 ? a->num_splits >= 8 : a->NG >= 4 * (int64_t)a->B;
+  const int rows_per_wg = wide ? mla::CombineShape<4>::kRowsPerWg : mla::CombineShape<1>::kRowsPerWg;
+  const int64_t blocks = (int64_t)a->B * a->nrb * (mla::kRowsPerBlock / rows_per_wg);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(mla::mla_combine_kernel, dim3((unsigned)blocks), dim3(mla::kThreads), 0, stream, *a);
+  if (wide)
+    hipLaunchKernelGGL(mla::mla_combine_kernel<4>, dim3((unsigned)blocks), dim3(mla::kThreads), 0, stream, *a);
+  else
+    hipLaunchKernelGGL(mla::mla_combine_kernel<1>, dim3((unsigned)blocks), dim3(mla::kThreads), 0, stream, *a);
   return hipGetLastError();
 }
 
