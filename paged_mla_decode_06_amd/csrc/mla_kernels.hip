@@ -1090,17 +1090,20 @@ __global__ __launch_bounds__(kThreads, kWaves == 1 ? 8 : 4) void mla_combine_ker
   const int row = rb * kRowsPerBlock + row_in_blk;
   const QExtent qe = q_extent<true>(a, b);
   if (row >= qe.qb * a.H) return;
-  const int32_t U = units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
   // the pieces of this row block: groups [g0, g1]
   int64_t g0, g1, first_pos = 0, total = 0;
   if (a.num_splits > 0) {
+    const int32_t U = units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
     const int32_t Sp = a.num_splits < U ? a.num_splits : U;
     if (Sp <= 1) return;
     g0 = (int64_t)b * a.num_splits;
     g1 = g0 + Sp - 1;
   } else {
+    // the request's cost positions give its tile count too (positions_of),
+    // so the three offsets load together and seq_lens is not read
     total = a.pos_off_ws[a.B];
     first_pos = a.pos_off_ws[b];
+    const int32_t U = a.pos_off_ws[b + 1] - (int32_t)first_pos - kPieceCost;
     g0 = first_group(first_pos, total, a.NG);
     g1 = last_group(first_pos, U, total, a.NG);
     if (g0 == g1) return;
