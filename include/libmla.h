@@ -49,7 +49,9 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+/* 2: adds mla_decode_qparts(_rope), mla_decode_ragged, mla_check_qo_indptr_host,
+ * mla_kv_append(_rope); version 1 entry points and structs are unchanged. */
+#define MLA_ABI_VERSION 2
 
 typedef enum {
   MLA_OK = 0,

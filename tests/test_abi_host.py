@@ -31,7 +31,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert mla.mla_abi_version() == 1
+    assert mla.mla_abi_version() == 2
     for code, name in [(0, "MLA_OK"), (1, "MLA_ERR_INVALID_VALUE"), (2, "MLA_ERR_NOT_SUPPORTED"),
                        (3, "MLA_ERR_WORKSPACE_TOO_SMALL"), (4, "MLA_ERR_HIP"), (99, "MLA_ERR_UNKNOWN")]:
         assert mla.status_name(code) == name
