@@ -366,8 +366,18 @@ struct Stage<false> {
   }
 };
 
+#ifndef MLA_F8_CVT_DIRECT
+#define MLA_F8_CVT_DIRECT 1
+#endif
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
+#if MLA_F8_CVT_DIRECT
+  // Two e4m3fn codes (the low or the high half of the word) straight to a
+  // bf16 pair by the gfx950 scaled conversion with scale 1: every e4m3fn
+  // value is a bf16 value, so the conversion is exact.
+  typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, (bf16x2_cvt_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, HI));
+#else
   // e4m3fn -> fp32 is exact; every e4m3fn value is a bf16 value, so keeping
   // the upper 16 bits of each fp32 is exact too.  The pair is taken as one
   // 64-bit value and packed with a byte permute: extracting the second float
@@ -375,6 +385,7 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
   // first one.
   const u32x2_t f = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_cvt_pk_f32_fp8((int)word, HI));
   return __builtin_amdgcn_perm(f[1], f[0], 0x07060302u);
+#endif
 }
 
 // fp8 pool: global -> registers (8 codes per chunk), converted once per tile
