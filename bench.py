@@ -96,8 +96,16 @@ def cpu_baseline(inp, budget_s: float = 10.0, rg=None):
     else:
         nbytes, _ = mla.algorithmic_work_ragged(lens, rg.q_lens[idx], inp.heads, inp.page_size, kv_bytes)
     passes = f", {done / inp.batch:.2f} passes over the batch" if done > inp.batch else ""
+    q_tokens = int(np.sum(rg.q_lens[idx])) if rg is not None else done * inp.q_len
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": orc.threads(), "kind": "oracle",
-            "seconds": round(t_total, 3),
+            "seconds": round(t_total, 3), "decode_tokens_per_s": round(q_tokens / t_total, 3),
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model,
             "sample": f"{done} whole requests in batch order{passes} (all their query rows, "
                       f"{int(lens.sum())} cached tokens), fp64 C oracle, OpenMP over query rows; "
                       f"rate = the sample's algorithmic bytes / its time"}
