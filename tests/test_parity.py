@@ -45,6 +45,11 @@ CASES = [
     ("fp8", 1, 128, 64, (1, 64, 65, 500)),
     ("fp8", 1, 16, 32, (0, 33, 100)),
     ("fp8", 4, 32, 64, (4, 70, 131)),
+    # the limits the library accepts: q_len * heads = 4096 query rows (64 row
+    # blocks per request), the longest q_len, the most heads
+    ("bf16", 16, 256, 64, (16, 100, 300)),
+    ("bf16", 64, 64, 32, (64, 65, 200)),
+    ("fp8", 1, 256, 64, (1, 500)),
 ]
 
 
@@ -115,10 +120,12 @@ def test_full_size_repeatable(name):
     assert not differing, f"{name}: {len(differing)} of 160 calls differ from the first, e.g. {differing[:3]}"
 
 
-@pytest.mark.parametrize("B", [700, 1500])
+@pytest.mark.parametrize("B", [700, 1024, 1025, 1500, 8192])
 def test_many_requests(orc, B):
     """Large batches of short requests, some empty: the workgroup plan is found
-    by one wave per workgroup up to 1024 requests and block-wide beyond."""
+    by one wave per workgroup up to 1024 requests and block-wide beyond (both
+    sides of that boundary are taken), up to 8192, the largest batch the
+    library accepts (its offsets then fill 32 KB of the tile buffers)."""
     rng = np.random.default_rng(50 + B)
     lens = rng.integers(0, 70, size=B)
     lens[::97] = 0
