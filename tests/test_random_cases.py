@@ -1,7 +1,11 @@
 """Seeded random decode configurations on the GPU against the oracle: batch,
 query length, head count, page size, ragged lengths (empty requests
 included), pool type and k_scale, split mode -- drawn per seed, so that
-combinations the hand-picked cases miss are covered too."""
+combinations the hand-picked cases miss are covered too.  The same draws
+drive ragged batches and the query read from two strided parts with the
+rotary embedding."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -11,10 +15,11 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
+import paged_mla_decode_06_amd as mla
 import oracle
-from oracle import ragged as RG
+from oracle import ragged as RG, rope as R
 import oracle_pins as P
-from mla_synth import ragged
+from mla_synth import ragged, rope_cache
 import gpu_util as G
 from test_ragged import run_ragged
 
@@ -54,3 +59,60 @@ def test_random_ragged(seed):
     o, l = run_ragged(rg, **kw)
     ro, rl = RG.decode(oracle.default(), rg)
     G.compare(o, l, ro, rl, fp8=inp.kv_fp8, what=f"ragged seed {seed}: q_lens={list(q_lens)} {kw}")
+
+
+def _padded_view(t, head_major, pad_w, extra, dev="cuda"):
+    """The values of t [T, H, W] as a strided view of a larger zero-filled
+    buffer: each row padded by pad_w elements and `extra` unused token rows
+    (or heads), tokens outermost or heads outermost."""
+    T, H, W = t.shape
+    if head_major:
+        buf = torch.zeros((H, T + extra, W + pad_w), dtype=t.dtype, device=dev)
+        v = buf[:, :T, :W].transpose(0, 1)
+    else:
+        buf = torch.zeros((T, H + extra, W + pad_w), dtype=t.dtype, device=dev)
+        v = buf[:, :H, :W]
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_query_parts(seed):
+    """The query as two strided parts (random padding, token- or head-major)
+    with or without the rotary embedding (either pairing), at random
+    positions, some outside the cos/sin cache (clamped): byte-identical to a
+    plain decode of the oracle-rotated query, and within tolerance of the
+    oracle's decode of it."""
+    inp, kw, r = _draw(300 + seed)
+    B, ql, H, _ = inp.q.shape
+    T = B * ql
+    rope = r.choice(["none", "neox", "interleaved"])
+    q, pool, bt, sl = G.to_device(inp)
+    qn = _padded_view(q[..., :512].reshape(T, H, 512), bool(r.random() < 0.5), 8 * int(r.integers(0, 4)),
+                      int(r.integers(0, 3)))
+    qr = _padded_view(q[..., 512:].reshape(T, H, 64), bool(r.random() < 0.5), 8 * int(r.integers(0, 9)),
+                      int(r.integers(0, 3)))
+    args = dict(max_seq_len=inp.max_seq_len, softmax_scale=inp.softmax_scale, k_scale=inp.k_scale, **kw)
+    out1 = torch.full((B, ql, H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse1 = torch.full((B, ql, H), float("nan"), dtype=torch.float32, device="cuda")
+    rq = inp.q
+    if rope == "none":
+        mla.mla_decode_qparts(qn, qr, pool, bt, sl, out1, lse1, **args)
+    else:
+        cache = rope_cache(int(inp.max_seq_len) + 8)
+        pos = r.integers(-3, cache.shape[0] + 3, size=(B, ql)).astype(np.int64)
+        mla.mla_decode_qparts(qn, qr, pool, bt, sl, out1, lse1,
+                              positions=torch.from_numpy(pos.reshape(-1)).cuda(),
+                              cos_sin_cache=torch.from_numpy(cache).cuda(), is_neox=rope == "neox", **args)
+        rq = R.rotate_query(inp.q, np.clip(pos, 0, cache.shape[0] - 1), cache, rope == "neox")
+    inp_r = dataclasses.replace(inp, q=rq)
+    out2 = torch.full_like(out1, float("nan"))
+    lse2 = torch.full_like(lse1, float("nan"))
+    mla.mla_decode(torch.from_numpy(rq.view(np.int16)).view(torch.bfloat16).cuda(), pool, bt, sl, out2, lse2,
+                   **args)
+    torch.cuda.synchronize()
+    what = f"seed {seed}: B={B} q={ql} H={H} fp8={inp.kv_fp8} rope={rope} strides={qn.stride()}/{qr.stride()} {kw}"
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)), f"{what}: outputs differ"
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32)), f"{what}: LSEs differ"
+    ro, rl = oracle.default().decode(inp_r)
+    G.compare(out1.float().cpu().numpy(), lse1.cpu().numpy(), ro, rl, fp8=inp.kv_fp8, what=what)
