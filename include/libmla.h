@@ -81,7 +81,10 @@ typedef struct {
   float k_scale;              /* fp8 pool: finite, > 0; bf16 pool: ignored */
   int32_t num_splits;         /* 0: the balanced planner; n > 0: split every request's token range into
                                  min(n, its 32-token tiles) pieces, one workgroup each (at most 1024) */
-  int32_t min_work_units;     /* balanced planner: 0 = one workgroup per compute unit; n > 0 = n workgroups */
+  int32_t min_work_units;     /* balanced planner: 0 = one workgroup per compute unit; n > 0 = n workgroups
+                                 (one decode workgroup fits a compute unit at a time, so a target above the
+                                 CU count runs in several rounds and is slower; it is there to force many
+                                 split pieces) */
   int32_t num_cus;            /* 0: read the compute-unit count of the current device; n > 0: use n
                                  (lets host-only planning calls run without a device) */
 } mla_decode_params;
