@@ -99,8 +99,6 @@ constexpr int kTileLoads = kChunks / 64;           // 36 wave-wide 1 KB loads pe
 constexpr int kLoadsPerWave = kTileLoads / kLoaderWaves;   // 9 per loader wave and tile
 constexpr int kQSteps = kRowDim / 32;              // 18 k-steps of 32 over the 576 dims
 constexpr int kVBlocks = kLatentDim / 16;          // 32 blocks of 16 latent dims
-constexpr int kFp8Chunks = kTile * kRowDim / 8;    // 2304 8-byte chunks per fp8 tile
-constexpr int kFp8PerThread = (kFp8Chunks + kLoaderThreads - 1) / kLoaderThreads;   // 9
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.6931471805599453f;
 // A row's running maximum is raised only when a tile's maximum exceeds it by
@@ -388,11 +386,19 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
 #endif
 }
 
-// fp8 pool: global -> registers (8 codes per chunk), converted once per tile
-// and stored to LDS as bf16.
+// fp8 pool: global -> registers, 16 codes (a 16-byte chunk, one of a row's 36)
+// per load, converted once per tile and stored to LDS as bf16: the two
+// 16-byte LDS chunks 2c and 2c+1 of the row.  A tile's 1152 chunks take
+// 4.5 loads per loader lane: the fifth only in loader waves 0 and 1.  The
+// rows of a tile are consecutive slots of one page, so chunk ci of the tile
+// is at byte 16*ci of its first row.
 template <>
 struct Stage<true> {
-  u32x2_t v[kFp8PerThread];
+  static constexpr int kChunks = kTile * kRowDim / 16;   // 1152
+  static constexpr int kRowChunks = kRowDim / 16;        // 36
+  static constexpr int kPer = (kChunks + kLoaderThreads - 1) / kLoaderThreads;   // 5
+  static_assert(kChunks % 64 == 0, "every loader wave loads whole or no chunks");
+  u32x4_t v[kPer];
   __device__ __forceinline__ void init(int) {}
   // Called by the loader waves; lt = thread index among them.
   __device__ __forceinline__ void load(const SplitArgs& a, PageWindow& pw, int b, int ts, int tok_end) {
@@ -403,27 +409,31 @@ struct Stage<true> {
       if ((uint32_t)page < (uint32_t)a.N) base = (const char*)a.pool + ((int64_t)page * a.P + (ts % a.P)) * kRowDim;
     }
 #pragma unroll
-    for (int i = 0; i < kFp8PerThread; i++) {
+    for (int i = 0; i < kPer; i++) {
       const int ci = lt + kLoaderThreads * i;
-      const int r = ci / 72, c = ci - r * 72;
-      u32x2_t x = {0u, 0u};
-      if (base != nullptr && ci < kFp8Chunks && ts + r < tok_end) x = *(const u32x2_t*)(base + r * kRowDim + c * 8);
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (base != nullptr && ci < kChunks && ts + ci / kRowChunks < tok_end) x = *(const u32x4_t*)(base + 16 * ci);
       v[i] = x;
     }
   }
   __device__ __forceinline__ void store(lds_char* buf) const {
     const int lt = threadIdx.x - 64 * kLoaderWave0;
 #pragma unroll
-    for (int i = 0; i < kFp8PerThread; i++) {
+    for (int i = 0; i < kPer; i++) {
       const int ci = lt + kLoaderThreads * i;
-      if (ci >= kFp8Chunks) continue;
-      const int r = ci / 72, c = ci - r * 72;
-      u32x4_t y;
-      y[0] = fp8x2_to_bf16x2<false>(v[i][0]);
-      y[1] = fp8x2_to_bf16x2<true>(v[i][0]);
-      y[2] = fp8x2_to_bf16x2<false>(v[i][1]);
-      y[3] = fp8x2_to_bf16x2<true>(v[i][1]);
-      *(__attribute__((address_space(3))) u32x4_t*)(buf + lds_off(r, c)) = y;
+      if (ci >= kChunks) continue;
+      const int r = ci / kRowChunks, c = 2 * (ci - r * kRowChunks);   // LDS chunks c and c + 1 of row r
+      u32x4_t y0, y1;
+      y0[0] = fp8x2_to_bf16x2<false>(v[i][0]);
+      y0[1] = fp8x2_to_bf16x2<true>(v[i][0]);
+      y0[2] = fp8x2_to_bf16x2<false>(v[i][1]);
+      y0[3] = fp8x2_to_bf16x2<true>(v[i][1]);
+      y1[0] = fp8x2_to_bf16x2<false>(v[i][2]);
+      y1[1] = fp8x2_to_bf16x2<true>(v[i][2]);
+      y1[2] = fp8x2_to_bf16x2<false>(v[i][3]);
+      y1[3] = fp8x2_to_bf16x2<true>(v[i][3]);
+      *(__attribute__((address_space(3))) u32x4_t*)(buf + lds_off(r, c)) = y0;
+      *(__attribute__((address_space(3))) u32x4_t*)(buf + lds_off(r, c + 1)) = y1;
     }
   }
 };
