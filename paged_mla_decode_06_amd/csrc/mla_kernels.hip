@@ -1098,22 +1098,60 @@ struct CombineShape {
 // One row per wave: at most 64 VGPRs, eight workgroups per CU, so the grid of
 // a full-size decode (up to 2048 workgroups) runs in one round.  One row per
 // workgroup: fewer, wider workgroups, up to 128 VGPRs.
-template <int kWaves>
+//
+// kByGroup (balanced plans with fewer groups than requests, B <= kByGroupMaxB):
+// the grid covers groups instead of requests, NG * nrb * 16 workgroups.  A
+// split request's last tile lies in the share of exactly one group g1, and
+// that share starts inside the request (its first tile lies in an earlier
+// group), so the request holding position start(g) is the only one the
+// workgroups of group g may have to merge: they merge it when it is split
+// and ends in g's share.  Unsplit requests then cost no workgroup.
+constexpr int kByGroupMaxB = 4 * kThreads;   // offsets found with one load round per thread
+template <int kWaves, bool kByGroup>
 __global__ __launch_bounds__(kThreads, kWaves == 1 ? 8 : 4) void mla_combine_kernel(CombineArgs a) {
   static_assert(kWaves == 1 || kWaves == kThreads / 64, "one wave per row, or the whole workgroup");
+  static_assert(!kByGroup || kWaves == 1, "the group grid uses one wave per row");
   constexpr int kRowsPerWg = CombineShape<kWaves>::kRowsPerWg;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ws = kWaves == 1 ? 0 : wave;       // this wave's share of the pieces
   const int chunks = kRowsPerBlock / kRowsPerWg;
-  const int64_t blk = blockIdx.x / chunks;     // b * nrb + rb
+  const int64_t blk = blockIdx.x / chunks;     // b * nrb + rb, or g * nrb + rb with kByGroup
   const int row_in_blk = (int)(blockIdx.x - blk * chunks) * kRowsPerWg + (kWaves == 1 ? wave : 0);
-  const int32_t b = (int32_t)(blk / a.nrb), rb = (int32_t)(blk - (int64_t)b * a.nrb);
+  int32_t b, rb;
+  int64_t g0, g1, first_pos = 0, total = 0;
+  if constexpr (kByGroup) {
+    // every wave of the workgroup takes part before any returns
+    const int64_t g = blk / a.nrb;
+    rb = (int32_t)(blk - g * a.nrb);
+    total = a.pos_off_ws[a.B];
+    const int64_t v = wg_start(g, total, a.NG);
+    __shared__ int32_t found;
+    if (threadIdx.x == 0) found = -1;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kByGroupMaxB / kThreads; k++) {
+      const int bb = (int)threadIdx.x + kThreads * k;
+      if (bb < a.B && a.pos_off_ws[bb] <= v && v < a.pos_off_ws[bb + 1]) found = bb;   // one request holds v
+    }
+    __syncthreads();
+    b = found;
+    if (b < 0) return;   // an empty share at the end
+    first_pos = a.pos_off_ws[b];
+    const int32_t U = a.pos_off_ws[b + 1] - (int32_t)first_pos - kPieceCost;
+    g0 = first_group(first_pos, total, a.NG);
+    g1 = last_group(first_pos, U, total, a.NG);
+    if (g1 != g || g0 == g1) return;   // not a split request that ends in this share
+  } else {
+    b = (int32_t)(blk / a.nrb);
+    rb = (int32_t)(blk - (int64_t)b * a.nrb);
+  }
   const int row = rb * kRowsPerBlock + row_in_blk;
   const QExtent qe = q_extent<true>(a, b);
   if (row >= qe.qb * a.H) return;
   // the pieces of this row block: groups [g0, g1]
-  int64_t g0, g1, first_pos = 0, total = 0;
-  if (a.num_splits > 0) {
+  if constexpr (kByGroup) {
+    // g0, g1, first_pos and total were found above
+  } else if (a.num_splits > 0) {
     const int32_t U = units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
     const int32_t Sp = a.num_splits < U ? a.num_splits : U;
     if (Sp <= 1) return;
@@ -1329,13 +1367,21 @@ hipError_t mla_launch_split(const mla::SplitArgs* a, int fp8, hipStream_t stream
 hipError_t mla_launch_combine(const mla::CombineArgs* a, hipStream_t stream) {
   // a workgroup per row when requests are split into many pieces on average
   const bool wide = a->num_splits > 0 ? a->num_splits >= 8 : a->NG >= 4 * (int64_t)a->B;
+  // the grid over groups when they are fewer than the requests
+  const bool by_group = !wide && a->num_splits == 0 && a->NG < a->B && a->B <= mla::kByGroupMaxB;
   const int rows_per_wg = wide ? mla::CombineShape<4>::kRowsPerWg : mla::CombineShape<1>::kRowsPerWg;
-  const int64_t blocks = (int64_t)a->B * a->nrb * (mla::kRowsPerBlock / rows_per_wg);
+  const int64_t units = by_group ? a->NG : (int64_t)a->B;
+  const int64_t blocks = units * a->nrb * (mla::kRowsPerBlock / rows_per_wg);
   if (blocks == 0) return hipSuccess;
   if (wide)
-    hipLaunchKernelGGL(mla::mla_combine_kernel<4>, dim3((unsigned)blocks), dim3(mla::kThreads), 0, stream, *a);
+    hipLaunchKernelGGL((mla::mla_combine_kernel<4, false>), dim3((unsigned)blocks), dim3(mla::kThreads), 0, stream,
+                       *a);
+  else if (by_group)
+    hipLaunchKernelGGL((mla::mla_combine_kernel<1, true>), dim3((unsigned)blocks), dim3(mla::kThreads), 0, stream,
+                       *a);
   else
-    hipLaunchKernelGGL(mla::mla_combine_kernel<1>, dim3((unsigned)blocks), dim3(mla::kThreads), 0, stream, *a);
+    hipLaunchKernelGGL((mla::mla_combine_kernel<1, false>), dim3((unsigned)blocks), dim3(mla::kThreads), 0, stream,
+                       *a);
   return hipGetLastError();
 }
 

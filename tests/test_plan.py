@@ -96,6 +96,44 @@ def test_balanced_plan_covers_and_balances(seed):
     assert part.max() <= 2
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_split_requests_end_in_distinct_group_shares(seed):
+    """What the combine's group grid relies on (plans with fewer groups than
+    requests): the last piece of every split request lies in a group g whose
+    share starts inside that request, after its first tile; so the request
+    holding a group's first position, if split and ending in that group, is
+    the only one the group's combine workgroups have to merge, and every
+    split request is merged by exactly one group."""
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(20, 1025))
+    q_len, H = int(rng.choice([1, 4])), int(rng.choice([16, 128]))
+    L = rng.integers(0, 9000, size=B).astype(np.int32)
+    L[rng.random(B) < 0.1] = 0
+    p = params(B, q_len, H, int(max(L.max(), 1)), num_cus=int(rng.choice([64, 256])))
+    pieces, grid = mla.mla_plan_host(p, L)
+    nrb = -(-q_len * H // mla.ROWS_PER_BLOCK)
+    NG, c = grid // nrb, mla.PIECE_COST
+    U = np.maximum(1, -(-np.clip(L, 0, p.max_seq_len) // mla.TILE)).astype(np.int64)
+    off = np.concatenate([[0], np.cumsum(U + c)])
+    T = int(off[-1])
+    start = [g * T // NG for g in range(NG)]
+    last_group = {}
+    n_pieces = {}
+    for wg, b, rb, t0, t1, slot in pieces:
+        if rb == 0:
+            n_pieces[b] = n_pieces.get(b, 0) + 1
+            if t1 == U[b]:
+                last_group[b] = wg // nrb
+    split = {b for b, n in n_pieces.items() if n > 1}
+    merged = []
+    for g in range(NG):
+        b = int(np.searchsorted(off, start[g], side="right") - 1)   # the request holding start(g)
+        if start[g] < T and b in split and last_group[b] == g:
+            assert off[b] + c < start[g], "the share starts after the request's first tile"
+            merged.append(b)
+    assert sorted(merged) == sorted(split)
+
+
 @pytest.mark.parametrize("S", [1, 2, 3, 7, 64])
 def test_forced_plan(S):
     L = np.array([0, 1, 31, 32, 33, 300, 4096], dtype=np.int32)
