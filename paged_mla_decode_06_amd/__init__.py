@@ -188,6 +188,29 @@ def alloc_workspace(p: mla_decode_params, device="cuda"):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
+def _check_decode_shapes(B: int, q_len: int, H: int, kv_pool, block_table, seq_lens, out, lse, max_seq_len: int,
+                         out_shape, lse_shape):
+    """Shape checks of a decode call, before any device work: the library
+    takes plain pointers, so a tensor smaller than the sizes the parameters
+    imply would be read or written past its end."""
+    import torch
+    if kv_pool.dim() != 3 or kv_pool.shape[-1] != ROW_DIM:
+        raise ValueError("kv_pool must be [num_pages, page_size, 576]")
+    if kv_pool.dtype not in (torch.bfloat16, torch.float8_e4m3fn, torch.uint8):
+        raise ValueError("kv_pool must be bfloat16, or float8_e4m3fn (or uint8 holding e4m3fn codes)")
+    if tuple(out.shape) != tuple(out_shape):
+        raise ValueError(f"out must be {list(out_shape)}, got {list(out.shape)}")
+    if lse is not None and tuple(lse.shape) != tuple(lse_shape):
+        raise ValueError(f"lse must be {list(lse_shape)}, got {list(lse.shape)}")
+    if seq_lens.numel() != B:
+        raise ValueError(f"seq_lens must hold {B} lengths, got {seq_lens.numel()}")
+    P = kv_pool.shape[1]
+    need = -(-int(max_seq_len) // P) if P > 0 else 0
+    if block_table.dim() != 2 or block_table.shape[0] < B or block_table.shape[1] < need:
+        raise ValueError(f"block_table must be [B, W] with at least {B} rows and W >= ceil(max_seq_len / "
+                         f"page_size) = {need}, got {list(block_table.shape)}")
+
+
 def mla_decode(q, kv_pool, block_table, seq_lens, out, lse=None, workspace=None, *, max_seq_len: int,
                softmax_scale: float, k_scale: float = 1.0, num_splits: int = 0, min_work_units: int = 0,
                stream=None, params: Optional[mla_decode_params] = None):
@@ -198,6 +221,11 @@ def mla_decode(q, kv_pool, block_table, seq_lens, out, lse=None, workspace=None,
     bf16; lse fp32 [B, q_len, H] or None; workspace uint8 (allocated here when
     None).  All on the GPU, contiguous.  Returns (out, lse)."""
     import torch
+    if q.dim() != 4 or q.shape[-1] != ROW_DIM:
+        raise ValueError("q must be [B, q_len, H, 576]")
+    B, ql, H, _ = q.shape
+    _check_decode_shapes(B, ql, H, kv_pool, block_table, seq_lens, out, lse, max_seq_len, (B, ql, H, LATENT_DIM),
+                         (B, ql, H))
     for name, t in (("q", q), ("kv_pool", kv_pool), ("block_table", block_table), ("seq_lens", seq_lens),
                     ("out", out)):
         if not t.is_cuda:
@@ -261,6 +289,11 @@ def mla_decode_qparts(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse=N
     positions (int64 [B*q_len]) and cos_sin_cache (float32 [max_pos, 64]) the
     rope part is first turned by the rotary embedding (mla_decode_qparts_rope)."""
     import torch
+    if out.dim() != 4 or out.shape[-1] != LATENT_DIM:
+        raise ValueError("out must be [B, q_len, H, 512]")
+    B, ql, H, _ = out.shape
+    _check_decode_shapes(B, ql, H, kv_pool, block_table, seq_lens, out, lse, max_seq_len, (B, ql, H, LATENT_DIM),
+                         (B, ql, H))
     for name, t in (("q_nope", q_nope), ("q_rope", q_rope), ("kv_pool", kv_pool), ("block_table", block_table),
                     ("seq_lens", seq_lens), ("out", out)):
         if not t.is_cuda:
@@ -311,6 +344,13 @@ def mla_decode_ragged(q, qo_indptr, kv_pool, block_table, seq_lens, out, lse=Non
     (qo_indptr int32 [B+1] on the GPU, at most max_q_len per request); out
     [T, H, 512] bf16, lse [T, H] fp32 or None.  Returns (out, lse)."""
     import torch
+    if q.dim() != 3 or q.shape[-1] != ROW_DIM:
+        raise ValueError("q must be [T, H, 576]")
+    T, H, _ = q.shape
+    _check_decode_shapes(seq_lens.numel(), max_q_len, H, kv_pool, block_table, seq_lens, out, lse, max_seq_len,
+                         (T, H, LATENT_DIM), (T, H))
+    if qo_indptr.numel() != seq_lens.numel() + 1:
+        raise ValueError("qo_indptr must hold B+1 offsets")
     for name, t in (("q", q), ("qo_indptr", qo_indptr), ("kv_pool", kv_pool), ("block_table", block_table),
                     ("seq_lens", seq_lens), ("out", out)):
         if not t.is_cuda:

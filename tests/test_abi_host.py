@@ -298,3 +298,74 @@ def test_rope_checks(L, rope, ok):
     assert st == mla.MLA_ERR_INVALID_VALUE
     assert L.mla_kv_append_rope(ctypes.byref(good_append()), fake, fake, fake, None, fake, None) == \
         mla.MLA_ERR_INVALID_VALUE
+
+
+def _decode_tensors(torch, B=3, ql=2, H=16, P=64, W=4):
+    return dict(q=torch.zeros((B, ql, H, 576), dtype=torch.bfloat16),
+                kv_pool=torch.zeros((10, P, 576), dtype=torch.bfloat16),
+                block_table=torch.zeros((B, W), dtype=torch.int32),
+                seq_lens=torch.zeros(B, dtype=torch.int32),
+                out=torch.zeros((B, ql, H, 512), dtype=torch.bfloat16),
+                lse=torch.zeros((B, ql, H), dtype=torch.float32))
+
+
+def _shape_mistakes(torch, B=3, ql=2, H=16, P=64):
+    # max_seq_len 200 needs ceil(200 / 64) = 4 block-table columns
+    return [
+        (dict(out=torch.zeros((B, ql, H, 256), dtype=torch.bfloat16)), "out must be"),
+        (dict(out=torch.zeros((B, ql, H - 1, 512), dtype=torch.bfloat16)), "out must be"),
+        (dict(lse=torch.zeros((B, ql), dtype=torch.float32)), "lse must be"),
+        (dict(seq_lens=torch.zeros(B + 1, dtype=torch.int32)), "seq_lens must hold"),
+        (dict(block_table=torch.zeros((B - 1, 4), dtype=torch.int32)), "block_table must be"),
+        (dict(block_table=torch.zeros((B, 3), dtype=torch.int32)), "block_table must be"),
+        (dict(kv_pool=torch.zeros((10, P, 576), dtype=torch.float32)), "kv_pool must be"),
+        (dict(kv_pool=torch.zeros((10, P, 512), dtype=torch.bfloat16)), "kv_pool must be"),
+    ]
+
+
+def test_decode_binding_checks_shapes_before_any_device_work():
+    """The library takes plain pointers, so the binding refuses tensors whose
+    shapes disagree with the sizes the call implies (a smaller out, lse,
+    seq_lens or block table would be accessed past its end)."""
+    torch = pytest.importorskip("torch")
+    kw = dict(max_seq_len=200, softmax_scale=0.07)
+    t = _decode_tensors(torch)
+    with pytest.raises(ValueError, match="GPU tensor"):   # well shaped: stops at the device check
+        mla.mla_decode(**t, **kw)
+    for change, msg in _shape_mistakes(torch):
+        with pytest.raises(ValueError, match=msg):
+            mla.mla_decode(**{**t, **change}, **kw)
+
+
+def test_qparts_binding_checks_shapes():
+    torch = pytest.importorskip("torch")
+    kw = dict(max_seq_len=200, softmax_scale=0.07)
+    t = _decode_tensors(torch)
+    q = t.pop("q")
+    t["q_nope"], t["q_rope"] = q[..., :512], q[..., 512:]
+    with pytest.raises(ValueError, match="GPU tensor"):
+        mla.mla_decode_qparts(**t, **kw)
+    for change, msg in _shape_mistakes(torch):
+        if msg == "out must be":
+            msg = "(out|lse) must be"   # here out fixes B, q_len and H: another head count fails at lse
+        with pytest.raises(ValueError, match=msg):
+            mla.mla_decode_qparts(**{**t, **change}, **kw)
+
+
+def test_ragged_binding_checks_shapes():
+    torch = pytest.importorskip("torch")
+    B, T, H = 3, 5, 16
+    kw = dict(max_q_len=2, max_seq_len=200, softmax_scale=0.07)
+    t = dict(q=torch.zeros((T, H, 576), dtype=torch.bfloat16), qo_indptr=torch.zeros(B + 1, dtype=torch.int32),
+             kv_pool=torch.zeros((10, 64, 576), dtype=torch.bfloat16),
+             block_table=torch.zeros((B, 4), dtype=torch.int32), seq_lens=torch.zeros(B, dtype=torch.int32),
+             out=torch.zeros((T, H, 512), dtype=torch.bfloat16), lse=torch.zeros((T, H), dtype=torch.float32))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        mla.mla_decode_ragged(**t, **kw)
+    for change, msg in [(dict(out=torch.zeros((T - 1, H, 512), dtype=torch.bfloat16)), "out must be"),
+                        (dict(lse=torch.zeros((T, H + 1), dtype=torch.float32)), "lse must be"),
+                        (dict(qo_indptr=torch.zeros(B, dtype=torch.int32)), "qo_indptr must hold"),
+                        (dict(block_table=torch.zeros((B, 2), dtype=torch.int32)), "block_table must be"),
+                        (dict(kv_pool=torch.zeros((10, 64, 576), dtype=torch.float16)), "kv_pool must be")]:
+        with pytest.raises(ValueError, match=msg):
+            mla.mla_decode_ragged(**{**t, **change}, **kw)
