@@ -15,9 +15,11 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import oracle
+from oracle import ragged as RG
 import oracle_pins as P
-from mla_synth import generate, WORKLOADS
+from mla_synth import generate, WORKLOADS, ragged
 import gpu_util as G
+from test_ragged import run_ragged
 
 
 @pytest.fixture(scope="module")
@@ -133,3 +135,26 @@ def test_many_requests(orc, B):
     ro, rl = orc.decode(inp)
     o, l = G.run(inp)
     G.compare(o, l, ro, rl, what=f"B={B}")
+
+
+def test_many_requests_fp8_multi_token(orc):
+    """1024 requests (the most the combine's group grid takes), fp8 cache,
+    two query tokens each, some empty: fewer groups than requests."""
+    rng = np.random.default_rng(52)
+    lens = rng.integers(0, 300, size=1024)
+    lens[::61] = 0
+    inp = P.small(kv="fp8", q_len=2, lens=tuple(int(x) for x in lens), heads=16, seed=53, k_scale=0.5)
+    o, l = G.run(inp)
+    ro, rl = orc.decode(inp)
+    G.compare(o, l, ro, rl, fp8=True, what="B=1024 fp8 q_len=2")
+
+
+def test_many_requests_ragged(orc):
+    """1000 ragged requests with 0 to 4 query tokens through the group grid."""
+    rng = np.random.default_rng(54)
+    lens = rng.integers(4, 400, size=1000)
+    inp = P.small(q_len=4, lens=tuple(int(x) for x in lens), heads=16, seed=55)
+    rg = ragged(inp, q_lens=rng.integers(0, 5, size=1000))
+    o, l = run_ragged(rg)
+    ro, rl = RG.decode(orc, rg)
+    G.compare(o, l, ro, rl, what="B=1000 ragged")
