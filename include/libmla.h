@@ -96,10 +96,16 @@ int32_t mla_abi_version(void);
 const char* mla_status_str(int32_t status);
 
 /* Bytes of device workspace mla_decode() needs for these parameters (split-KV
- * partial results and planning scratch).  No device memory is touched; with
- * num_cus == 0 and min_work_units == 0 and num_splits == 0 it queries the
- * current device's compute-unit count.  The workspace needs no
- * initialisation. */
+ * partial results and planning scratch).  This is the split-KV workspace the
+ * pages hand their decode kernel: the zeroed buffer of
+ * get_trtllm_workspace_buffer on "tokenspeed trtllm_mla.py" and of
+ * TRTLLMMLABackend.__init__ on "sglang trtllm_mla_backend.py"
+ * (workspace_buffer).  Unlike theirs it is sized per call and needs no
+ * initialisation: it holds no counters, and every byte a call reads it has
+ * written first.  No device memory is touched; with num_cus == 0 and
+ * min_work_units == 0 and num_splits == 0 it queries the current device's
+ * compute-unit count.  Errors: MLA_ERR_INVALID_VALUE / MLA_ERR_NOT_SUPPORTED
+ * as mla_decode() for bad parameters, MLA_ERR_HIP if the device query fails. */
 mla_status mla_decode_workspace_size(const mla_decode_params* p, size_t* bytes);
 
 /* The decode.  Layouts (all row-major, contiguous):
@@ -158,9 +164,14 @@ mla_status mla_decode_qparts(const mla_decode_params* p, const void* q_nope, con
  * workspace: mla_decode_workspace_size(p) applies unchanged).
  *   q          device, bf16  [total_q_tokens][H][576]
  *   qo_indptr  device, int32 [B+1], nondecreasing, qo_indptr[0] = 0,
- *              qo_indptr[B] = total_q_tokens.  A request whose offsets
- *              fall outside [0, total_q_tokens] or run backwards is treated
- *              as having no query tokens (nothing is read or written for it).
+ *              qo_indptr[B] = total_q_tokens.  The offsets are trusted on
+ *              the device, never followed out of the tensors: a request whose
+ *              offsets fall outside [0, total_q_tokens] or run backwards is
+ *              treated as having no query tokens, and a request with more
+ *              than p->q_len tokens as having its first p->q_len; nothing is
+ *              read or written for the tokens left out, so their out and lse
+ *              rows keep whatever they held.  mla_check_qo_indptr_host()
+ *              checks the offsets on a host copy.
  *   out        device, bf16  [total_q_tokens][H][512]   (written)
  *   lse        device, fp32  [total_q_tokens][H], or NULL
  * Other arguments, layouts and errors as mla_decode().  With every q_b equal
@@ -221,7 +232,13 @@ mla_status mla_gather_kv(const mla_decode_params* p, const void* kv_pool, const 
                          const int32_t* seq_lens, int32_t b, void* dst, void* stream);
 
 /* Host mirror of the work plan (CPU only, no device access when p->num_cus >
- * 0 or p->min_work_units > 0 or p->num_splits > 0).  A plan assigns each
+ * 0 or p->min_work_units > 0 or p->num_splits > 0).  The plan plays the part
+ * of the tile-scheduler metadata and split counts the pages obtain from
+ * get_mla_metadata(seq_lens, heads, 1) in FlashMLABackend._init_decode_metadata
+ * on "tokenspeed flashmla.py"; here it is recomputed inside the decode kernel
+ * from the device seq_lens, and this call returns the same plan on the host
+ * for tests.  It lists pieces rather than the pages' per-request split
+ * pointer, because one workgroup may take pieces of two requests.  A plan assigns each
  * workgroup g < grid a list of pieces (g, b, row_block, tile_begin,
  * tile_end, slot): rows [64*row_block, 64*row_block+64) of request b's
  * q_len*H query rows (row = j*H + h) over 32-token tiles [tile_begin,

@@ -338,11 +338,18 @@ def mla_decode_qparts(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse=N
 def mla_decode_ragged(q, qo_indptr, kv_pool, block_table, seq_lens, out, lse=None, workspace=None, *,
                       max_q_len: int, max_seq_len: int, softmax_scale: float, k_scale: float = 1.0,
                       num_splits: int = 0, min_work_units: int = 0, stream=None,
-                      params: Optional[mla_decode_params] = None):
+                      params: Optional[mla_decode_params] = None, validate: bool = False):
     """Ragged multi-token decode: request b's query tokens are rows
     qo_indptr[b] .. qo_indptr[b+1]-1 of the packed q [T, H, 576] bf16
     (qo_indptr int32 [B+1] on the GPU, at most max_q_len per request); out
-    [T, H, 512] bf16, lse [T, H] fp32 or None.  Returns (out, lse)."""
+    [T, H, 512] bf16, lse [T, H] fp32 or None.  Returns (out, lse).
+
+    The library trusts the offsets on the device: a request whose offsets
+    fall outside [0, T] or run backwards gets no query token, and a request
+    with more than max_q_len tokens only its first max_q_len; the out/lse
+    rows of the tokens left out are not written.  validate=True copies the
+    offsets to the host first (a synchronisation) and raises MlaError
+    (MLA_ERR_INVALID_VALUE) unless they pass mla_check_qo_indptr_host."""
     import torch
     if q.dim() != 3 or q.shape[-1] != ROW_DIM:
         raise ValueError("q must be [T, H, 576]")
@@ -377,6 +384,9 @@ def mla_decode_ragged(q, qo_indptr, kv_pool, block_table, seq_lens, out, lse=Non
     p = params if params is not None else make_params(
         B, max_q_len, H, P, N, block_table.stride(0) if block_table.dim() == 2 else 1, max_seq_len,
         MLA_KV_FP8_E4M3FN if fp8 else MLA_KV_BF16, softmax_scale, k_scale, num_splits, min_work_units)
+    if validate:
+        ind_host = qo_indptr.cpu().numpy()
+        _check(mla_check_qo_indptr_host(p, ind_host, T), "mla_decode_ragged: qo_indptr")
     if workspace is None:
         workspace = alloc_workspace(p, q.device)
     st = lib().mla_decode_ragged(ctypes.byref(p), _ptr(q), _ptr(qo_indptr), int(T), _ptr(kv_pool),

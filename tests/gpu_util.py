@@ -56,6 +56,13 @@ def compare(o, l, ref_o, ref_l, fp8=False, what=""):
     return err / max(scale, 1e-30)
 
 
+def lse_err(l, ref_l):
+    """max |lse - ref| over the rows whose reference LSE is finite (0 if none)."""
+    ref_l = np.asarray(ref_l)
+    fin = ~np.isneginf(ref_l)
+    return float(np.max(np.abs(np.asarray(l)[fin] - ref_l[fin]))) if fin.any() else 0.0
+
+
 def _mismatch_report(o, l, ref_o, ref_l, bound):
     """Where the output is off: the leading indices (everything but the last,
     512-wide axis) of the rows over the bound, the span of dims involved, and

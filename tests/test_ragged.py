@@ -92,3 +92,47 @@ def test_full_size_draft_extend_sampled():
     ro, rl = RG.decode_rows(oracle.default(), rg, sel)
     G.compare(np.stack([o[t, h] for t, h in sel]), np.array([l[t, h] for t, h in sel]), ro, rl,
               what="draft_extend")
+
+
+def test_full_size_draft_extend_whole():
+    """The whole draft-extend batch (every packed query row and head) against
+    the fp64 oracle, in the launch configuration the benchmark times."""
+    rg = ragged(generate("draft_extend"))
+    o, l = run_ragged(rg)
+    ro, rl = RG.decode(oracle.default(), rg)
+    rel = G.compare(o, l, ro, rl, what="draft_extend")
+    print(f"draft_extend: {o.shape[0] * o.shape[1]} rows, max|gpu-oracle|/max|oracle| = {rel:.3e}, "
+          f"max|lse err| = {G.lse_err(l, rl):.3e}")
+
+
+def test_offsets_beyond_max_q_len_leave_rows_untouched():
+    """A request with more query tokens than max_q_len: its first max_q_len
+    tokens are decoded (as if it had that many), the rows of the rest are not
+    written; validate=True rejects the offsets before any device work."""
+    inp = P.small(kv="bf16", q_len=5, heads=16, page_size=32, lens=(40, 90), seed=212)
+    rg = ragged(inp, q_lens=[5, 2])          # request 0 has 5 tokens, max_q_len below is 4
+    _, pool, bt, sl = G.to_device(inp)
+    T, H, _ = rg.q.shape
+    q = torch.from_numpy(rg.q.view(np.int16)).view(torch.bfloat16).cuda()
+    ind = torch.from_numpy(rg.qo_indptr).cuda()
+    out = torch.full((T, H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    args = dict(max_q_len=4, max_seq_len=inp.max_seq_len, softmax_scale=inp.softmax_scale)
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_decode_ragged(q, ind, pool, bt, sl, out, lse, validate=True, **args)
+    assert e.value.status == mla.MLA_ERR_INVALID_VALUE
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all(), "a rejected call writes nothing"
+    mla.mla_decode_ragged(q, ind, pool, bt, sl, out, lse, **args)
+    torch.cuda.synchronize()
+    o, l = out.float().cpu().numpy(), lse.cpu().numpy()
+    assert np.isnan(o[4]).all() and np.isnan(l[4]).all(), "the token past max_q_len must stay unwritten"
+    # the first four tokens of request 0 are decoded as a 4-token request of
+    # the same length: token j sees t < L - 4 + 1 + j
+    v = RG.request_view(rg, 0)
+    v.q = np.ascontiguousarray(v.q[:, :4])
+    v.q_len = 4
+    ro, rl = oracle.default().decode(v)
+    G.compare(o[:4], l[:4], ro[0], rl[0], what="request 0, first four tokens")
+    ro1, rl1 = RG.decode(oracle.default(), rg)
+    G.compare(o[5:], l[5:], ro1[5:], rl1[5:], what="request 1")
