@@ -215,6 +215,24 @@ mla_status mla_decode_qparts_rope(const mla_decode_params* p, const void* q_nope
                                   const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * mla_decode() with its workspace in a device array the library holds
+ * itself, MLA_NOALLOC_SCRATCH_BYTES (64 MiB) per device, alive until the
+ * process ends.  The caller passes inputs and outputs as for mla_decode()
+ * (same layouts and errors); the call allocates nothing and frees nothing.
+ * Parameters whose workspace (mla_decode_workspace_size) exceeds the array
+ * return MLA_ERR_WORKSPACE_TOO_SMALL and enqueue nothing; every balanced plan
+ * sized to the compute-unit count fits (about 42 MB at most on 256 CUs).
+ * Every call on one device shares that device's array, so calls that may
+ * overlap on one device (two streams, two threads) race: serialise them.
+ * The array needs no clearing between calls: a call writes every byte of it
+ * it reads.  Results are bit-identical to mla_decode(). */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+mla_status mla_decode_noalloc(const mla_decode_params* p, const void* q, const void* kv_pool,
+                              const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                              void* stream);
+
 /* mla_decode() that also records three caller-created HIP events (hipEvent_t,
  * each may be NULL) on `stream`: before the split-KV kernel, between it and
  * the combine kernel, and after the combine, so that a benchmark can time the

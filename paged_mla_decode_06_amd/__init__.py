@@ -109,6 +109,8 @@ def lib() -> ctypes.CDLL:
         L.mla_kv_append_rope.restype = ctypes.c_int
         L.mla_kv_append_rope.argtypes = [ctypes.POINTER(mla_kv_append_params), vp, vp, vp, ctypes.POINTER(mla_rope),
                                          vp, vp]
+        L.mla_decode_noalloc.restype = ctypes.c_int
+        L.mla_decode_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         L.mla_kv_append.restype = ctypes.c_int
         L.mla_kv_append.argtypes = [ctypes.POINTER(mla_kv_append_params), vp, vp, vp, vp, vp]
         _lib = L
@@ -248,6 +250,44 @@ def mla_decode(q, kv_pool, block_table, seq_lens, out, lse=None, workspace=None,
                           _ptr(lse), _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                           _stream_handle(stream))
     _check(st, "mla_decode")
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MLA_NOALLOC_SCRATCH_BYTES
+
+
+def mla_decode_noalloc(q, kv_pool, block_table, seq_lens, out, lse=None, *, max_seq_len: int,
+                       softmax_scale: float, k_scale: float = 1.0, num_splits: int = 0, min_work_units: int = 0,
+                       stream=None, params: Optional[mla_decode_params] = None):
+    """mla_decode with the library's own per-device workspace array: nothing
+    is allocated, here or in the library (for graph capture and loops that
+    cannot allocate).  Calls that overlap on one device race on that array.
+    Same tensors and checks as mla_decode.  Returns (out, lse)."""
+    import torch
+    if q.dim() != 4 or q.shape[-1] != ROW_DIM:
+        raise ValueError("q must be [B, q_len, H, 576]")
+    B, ql, H, _ = q.shape
+    _check_decode_shapes(B, ql, H, kv_pool, block_table, seq_lens, out, lse, max_seq_len, (B, ql, H, LATENT_DIM),
+                         (B, ql, H))
+    for name, t in (("q", q), ("kv_pool", kv_pool), ("block_table", block_table), ("seq_lens", seq_lens),
+                    ("out", out)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    if not (q.is_contiguous() and kv_pool.is_contiguous() and out.is_contiguous() and seq_lens.is_contiguous()):
+        raise ValueError("q, kv_pool, seq_lens and out must be contiguous")
+    if block_table.stride(-1) != 1:
+        raise ValueError("block_table rows must be contiguous")
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise ValueError("q and out must be bfloat16")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32")
+    p = params if params is not None else params_for(q, kv_pool, block_table, max_seq_len, softmax_scale, k_scale,
+                                                     num_splits, min_work_units)
+    st = lib().mla_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(kv_pool), _ptr(block_table), _ptr(seq_lens),
+                                  _ptr(out), _ptr(lse), _stream_handle(stream))
+    _check(st, "mla_decode_noalloc")
     return out, lse
 
 

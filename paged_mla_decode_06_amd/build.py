@@ -14,7 +14,7 @@ LIB = os.path.join(HERE, "libmla.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["mla_kernels.hip", "mla_append.hip", "mla_api.cpp"]
+SOURCES = ["mla_kernels.hip", "mla_append.hip", "mla_noalloc.hip", "mla_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", INCLUDE, "-I", CSRC,
           # no packed fp32 instructions in any device code
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
