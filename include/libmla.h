@@ -174,6 +174,8 @@ mla_status mla_decode_qparts(const mla_decode_params* p, const void* q_nope, con
  *              checks the offsets on a host copy.
  *   out        device, bf16  [total_q_tokens][H][512]   (written)
  *   lse        device, fp32  [total_q_tokens][H], or NULL
+ * total_q_tokens = 0 (every request without a query token) checks the
+ * parameters and enqueues nothing; q, out and lse may then be NULL.
  * Other arguments, layouts and errors as mla_decode().  With every q_b equal
  * to p->q_len the results are bit-identical to mla_decode(). */
 mla_status mla_decode_ragged(const mla_decode_params* p, const void* q, const int32_t* qo_indptr,

@@ -8,6 +8,7 @@
 // (TRTLLMMLABackend.__init__ rejects page sizes other than 32 and 64).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -242,6 +243,9 @@ static mla_status decode_impl(const mla_decode_params* p, const QueryParts& qp, 
   a.R = p->q_len * p->num_heads;
   a.num_splits = p->num_splits;
   a.NG = lay.groups;
+  a.p_shift = p->page_size == 64 ? 6 : 5;
+  a.vg_per = mla::fold_factor(lay.groups, a.nrb, p->num_splits, di.cus);
+  a.NGL = mla::launched_groups(lay.groups, a.vg_per);
   a.scale_log2 = (float)((double)p->softmax_scale * (double)kscale * 1.4426950408889634);
   a.out_scale = kscale;
   hipStream_t st = (hipStream_t)stream;
@@ -287,6 +291,7 @@ mla_status mla_decode_ragged(const mla_decode_params* p, const void* q, const in
   if (p == nullptr) return MLA_ERR_INVALID_VALUE;
   if (total_q_tokens < 0 || (p->batch > 0 && qo_indptr == nullptr)) return MLA_ERR_INVALID_VALUE;
   if ((((uintptr_t)qo_indptr) & 3) != 0) return MLA_ERR_INVALID_VALUE;
+  if (total_q_tokens == 0) return check_params(p);   // no query token: nothing to write, q and out may be null
   QueryParts qp;
   qp.nope = q;
   qp.rope = q == nullptr ? nullptr : (const void*)((const uint16_t*)q + kLatentDim);
@@ -411,13 +416,21 @@ mla_status mla_plan_host(const mla_decode_params* p, const int32_t* seq_lens_hos
     };
     auto units = [&](int32_t b) -> int32_t { return mla::units_of(mla::clamp_len(seq_lens_host[b], p->max_seq_len)); };
     const int64_t total = off[(size_t)B];
-    for (int64_t g = 0; g < NG; g++) {
-      const int64_t v_begin = mla::wg_start(g, total, NG);
+    // The groups are walked as a folded launch on num_cus CUs (256 when
+    // unset) walks them, several per workgroup; the pieces do not depend on
+    // it.  They are listed by plan workgroup.
+    const int32_t vg = mla::fold_factor(NG, nrb, 0, p->num_cus > 0 ? p->num_cus : 256);
+    std::vector<std::pair<int64_t, mla::Piece>> got;
+    for (int64_t g0 = 0; g0 < NG; g0 += vg) {
+      const int64_t g1 = std::min<int64_t>(g0 + vg, NG);
+      const int64_t v_begin = mla::wg_start(g0, total, NG);
       const int32_t b_first = v_begin < total ? fr(v_begin) : 0;
       for (int32_t rb = 0; rb < nrb; rb++)
-        mla::balanced_pieces(g, NG, rb, nrb, total, b_first, off[(size_t)b_first], units,
-                             [&](const mla::Piece& pc) { emit(pc, g * nrb + rb); });
+        mla::folded_balanced_pieces(g0, g1, NG, rb, nrb, total, b_first, off[(size_t)b_first], units,
+                                    [&](const mla::Piece& pc, int64_t g) { got.emplace_back(g * nrb + rb, pc); });
     }
+    std::stable_sort(got.begin(), got.end(), [](const auto& x, const auto& y) { return x.first < y.first; });
+    for (const auto& e : got) emit(e.second, e.first);
   }
   *n_pieces = (int32_t)n;
   *grid = (int32_t)lay.wgs;
@@ -437,8 +450,10 @@ mla_status mla_plan_device(const mla_decode_params* p, const int32_t* seq_lens, 
   s = device_info(&di);
   if (s != MLA_OK) return s;
   if (!di.gfx950) return MLA_ERR_NOT_SUPPORTED;
-  if (mla_launch_plan(seq_lens, p->batch, p->max_seq_len, mla::row_blocks(p->q_len, p->num_heads), p->num_splits,
-                      lay.groups, max_per_wg, pieces, counts, (hipStream_t)stream) != hipSuccess)
+  const int32_t nrb = mla::row_blocks(p->q_len, p->num_heads);
+  if (mla_launch_plan(seq_lens, p->batch, p->max_seq_len, nrb, p->num_splits, lay.groups,
+                      mla::fold_factor(lay.groups, nrb, p->num_splits, di.cus), max_per_wg, pieces, counts,
+                      (hipStream_t)stream) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }

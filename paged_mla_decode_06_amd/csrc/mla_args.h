@@ -25,7 +25,10 @@ struct SplitArgs {
   const float* rope_cs;     // [rope_max_pos][64] fp32: cos 0..31, sin 32..63
   int32_t rope_max_pos, rope_neox;
   int32_t B, q_len, H, P, W, N, max_seq_len, nrb, R, num_splits;
-  int64_t NG;   // groups of the plan
+  int32_t p_shift;          // log2(P)
+  int32_t vg_per;           // plan groups walked by each launched group (balanced mode), else 1
+  int64_t NG;               // groups of the plan
+  int64_t NGL;              // groups of the launch: ceil(NG / vg_per)
   float scale_log2;         // softmax_scale * (k_scale for fp8) * log2(e)
   float out_scale;          // k_scale for fp8, else 1
 };
@@ -68,7 +71,8 @@ hipError_t mla_launch_gather(const void* pool, const int32_t* bt, const int32_t*
                              int32_t N, int32_t max_seq_len, int32_t b, int32_t elem_bytes, void* dst,
                              hipStream_t stream);
 hipError_t mla_launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t nrb, int32_t num_splits,
-                           int64_t G, int32_t max_per_wg, int32_t* pieces, int32_t* counts, hipStream_t stream);
+                           int64_t G, int32_t vg_per, int32_t max_per_wg, int32_t* pieces, int32_t* counts,
+                           hipStream_t stream);
 size_t mla_split_lds_bytes(int32_t B, int32_t num_splits);
 hipError_t mla_launch_append(const mla::AppendArgs* a, hipStream_t stream);
 }

@@ -328,9 +328,9 @@ struct Stage<false> {
             u32x4_t{0u, 0u, 0u, 0u};
       return 0;
     }
-    const int32_t page = pw.page(a, b, ts / a.P);
+    const int32_t page = pw.page(a, b, ts >> a.p_shift);
     const int32_t pg = (uint32_t)page < (uint32_t)a.N ? page : 0;
-    const char* base = (const char*)a.pool + ((int64_t)pg * a.P + (ts % a.P)) * (int64_t)kRowBytes;
+    const char* base = (const char*)a.pool + (((int64_t)pg << a.p_shift) + (ts & (a.P - 1))) * (int64_t)kRowBytes;
     const uint32_t dst = (uint32_t)(uintptr_t)(buf + wave * 1024);
     // Opaque copies: the offsets are unpacked here, once per tile, instead of
     // being hoisted out of the tile loop as nine live registers.
@@ -405,8 +405,9 @@ struct Stage<true> {
     const int lt = threadIdx.x - 64 * kLoaderWave0;
     const char* base = nullptr;
     if (ts < tok_end) {
-      const int32_t page = pw.page(a, b, ts / a.P);
-      if ((uint32_t)page < (uint32_t)a.N) base = (const char*)a.pool + ((int64_t)page * a.P + (ts % a.P)) * kRowDim;
+      const int32_t page = pw.page(a, b, ts >> a.p_shift);
+      if ((uint32_t)page < (uint32_t)a.N)
+        base = (const char*)a.pool + (((int64_t)page << a.p_shift) + (ts & (a.P - 1))) * kRowDim;
     }
 #pragma unroll
     for (int i = 0; i < kPer; i++) {
@@ -701,7 +702,7 @@ __device__ void load_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, c
   const int tok_end = min(pc.tile1 * kTile, L);
   const int nt = pc.tile1 - pc.tile0;
   PageWindow pw;
-  pw.init(a, b, (pc.tile0 * kTile) / a.P, (tok_end + a.P - 1) / a.P);
+  pw.init(a, b, (pc.tile0 * kTile) >> a.p_shift, (tok_end + a.P - 1) >> a.p_shift);
   if constexpr (FP8) {
 #if MLA_F8_DEFER
     // fp8 codes go through registers: tile t's codes are loaded in interval
@@ -1003,6 +1004,7 @@ __device__ __forceinline__ int32_t find_request(const int32_t* off, int32_t B, i
 
 // Every wave of a workgroup walks the same pieces: the loader waves fill the
 // tile ring, the compute waves consume it; their barriers pair up one to one.
+// grp: the first plan group of the launched group (forced mode: its only one).
 template <bool FP8, bool RAGGED, class PieceFn>
 __device__ __forceinline__ void for_each_piece(const SplitArgs& a, int64_t grp, int32_t rb, int32_t total,
                                                int32_t b_first, int32_t off_first, PieceFn&& fn_all) {
@@ -1020,7 +1022,9 @@ __device__ __forceinline__ void for_each_piece(const SplitArgs& a, int64_t grp, 
     return;
   }
   auto units = [&](int32_t b) -> int32_t { return units_of(clamp_len(a.seq_lens[b], a.max_seq_len)); };
-  balanced_pieces(grp, a.NG, rb, a.nrb, total, b_first, off_first, units, fn);
+  const int64_t g1 = min(grp + a.vg_per, a.NG);
+  folded_balanced_pieces(grp, g1, a.NG, rb, a.nrb, total, b_first, off_first, units,
+                         [&](const Piece& pc, int64_t) { fn(pc); });
 }
 
 // RAGGED: per-request query lengths from a.qo_indptr (a separate
@@ -1029,9 +1033,10 @@ template <bool FP8, bool RAGGED>
 __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   lds_char* tiles = (lds_char*)smem;
-  int64_t grp;
+  int64_t lgrp;
   int32_t rb;
-  group_of_block(blockIdx.x, a.nrb, &grp, &rb);
+  group_of_block(blockIdx.x, a.nrb, &lgrp, &rb);
+  const int64_t grp = lgrp * a.vg_per;   // the first plan group this workgroup walks
   // Balanced mode: the cost-position offsets of all requests, of which this workgroup
   // keeps only where its share starts; block 0 publishes them for the
   // combine.  Up to 64 * kWaveScanPer requests every wave computes them on its
@@ -1060,7 +1065,7 @@ __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a
       __syncthreads();   // every wave has read the offsets before tiles land there
     }
   }
-  if (grp >= a.NG) return;
+  if (lgrp >= a.NGL) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave >= kLoaderWave0) {
     if (MLA_PRIO_LD) __builtin_amdgcn_s_setprio(MLA_PRIO_LD);
@@ -1295,19 +1300,29 @@ __global__ __launch_bounds__(kThreads) void mla_gather_kernel(const void* pool, 
 }
 
 // ---- debug: the plan as the decode kernel computes it
+// (launched as the decode is: vg_per plan groups per launched group)
 __global__ __launch_bounds__(kThreads) void mla_plan_kernel(const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
                                                              int32_t nrb, int32_t num_splits, int64_t NG,
-                                                             int32_t max_per_wg, int32_t* pieces,
-                                                             int32_t* counts) {
+                                                             int32_t vg_per, int64_t NGL, int32_t max_per_wg,
+                                                             int32_t* pieces, int32_t* counts) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int32_t* off = (int32_t*)smem;
-  int64_t grp;
+  int64_t lgrp;
   int32_t rb;
-  group_of_block(blockIdx.x, nrb, &grp, &rb);
-  const int64_t wg = grp * nrb + rb;      // logical workgroup index of the plan
+  group_of_block(blockIdx.x, nrb, &lgrp, &rb);
+  const int64_t grp = lgrp * vg_per;
+  // Pieces are counted per plan group: cur is the group being counted (its
+  // n pieces so far), every group below it already has its count written.
+  int64_t cur = grp;
   int32_t n = 0;
-  auto emit = [&](const Piece& pc) {
+  auto close_until = [&](int64_t g) {   // write the counts of groups cur .. g-1, then count g
+    for (; cur < g; cur++, n = 0)
+      if (threadIdx.x == 0) counts[cur * nrb + rb] = n;
+  };
+  auto emit = [&](const Piece& pc, int64_t g) {
+    close_until(g);
     if (threadIdx.x == 0 && n < max_per_wg) {
+      const int64_t wg = g * nrb + rb;   // logical workgroup index of the plan
       int32_t* o = pieces + (wg * max_per_wg + n) * 6;
       o[0] = (int32_t)wg; o[1] = pc.b; o[2] = pc.rb; o[3] = pc.tile0; o[4] = pc.tile1; o[5] = pc.slot;
     }
@@ -1315,19 +1330,20 @@ __global__ __launch_bounds__(kThreads) void mla_plan_kernel(const int32_t* seq_l
   };
   __shared__ int32_t part[kThreads];
   if (num_splits == 0) build_pos_offsets<kThreads>(seq_lens, B, max_seq_len, off, part);
-  if (grp >= NG) return;
+  if (lgrp >= NGL) return;
+  const int64_t g1 = min(grp + vg_per, NG);
   if (num_splits > 0) {
     const int32_t b = (int32_t)(grp / num_splits);
     Piece pc;
-    if (forced_piece(grp, rb, nrb, num_splits, units_of(clamp_len(seq_lens[b], max_seq_len)), &pc)) emit(pc);
+    if (forced_piece(grp, rb, nrb, num_splits, units_of(clamp_len(seq_lens[b], max_seq_len)), &pc)) emit(pc, grp);
   } else {
     const int32_t total = off[B];
     const int64_t v_begin = wg_start(grp, total, NG);
     const int32_t b_first = v_begin < total ? find_request(off, B, v_begin) : 0;
     auto units = [&](int32_t b) -> int32_t { return units_of(clamp_len(seq_lens[b], max_seq_len)); };
-    balanced_pieces(grp, NG, rb, nrb, total, b_first, off[b_first], units, emit);
+    folded_balanced_pieces(grp, g1, NG, rb, nrb, total, b_first, off[b_first], units, emit);
   }
-  if (threadIdx.x == 0) counts[wg] = n;
+  close_until(g1);
 }
 
 }  // namespace mla
@@ -1359,7 +1375,7 @@ hipError_t mla_launch_split(const mla::SplitArgs* a, int fp8, hipStream_t stream
     if (e != hipSuccess) return e;
     attr_set[v] = true;
   }
-  const unsigned grid = (unsigned)mla::launch_grid(a->NG, a->nrb);
+  const unsigned grid = (unsigned)mla::launch_grid(a->NGL, a->nrb);
   hipLaunchKernelGGL(fns[v], dim3(grid), dim3(mla::kSplitThreads), lds, stream, *a);
   return hipGetLastError();
 }
@@ -1398,10 +1414,12 @@ hipError_t mla_launch_gather(const void* pool, const int32_t* bt, const int32_t*
 }
 
 hipError_t mla_launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t nrb, int32_t num_splits,
-                           int64_t NG, int32_t max_per_wg, int32_t* pieces, int32_t* counts, hipStream_t stream) {
+                           int64_t NG, int32_t vg_per, int32_t max_per_wg, int32_t* pieces, int32_t* counts,
+                           hipStream_t stream) {
   const size_t lds = num_splits > 0 ? 16 : ((size_t)B + 1) * 4;
-  hipLaunchKernelGGL(mla::mla_plan_kernel, dim3((unsigned)mla::launch_grid(NG, nrb)), dim3(mla::kThreads), lds, stream,
-                     seq_lens, B, max_seq_len, nrb, num_splits, NG, max_per_wg, pieces, counts);
+  const int64_t NGL = mla::launched_groups(NG, vg_per);
+  hipLaunchKernelGGL(mla::mla_plan_kernel, dim3((unsigned)mla::launch_grid(NGL, nrb)), dim3(mla::kThreads), lds,
+                     stream, seq_lens, B, max_seq_len, nrb, num_splits, NG, vg_per, NGL, max_per_wg, pieces, counts);
   return hipGetLastError();
 }
 

@@ -103,7 +103,8 @@ struct Piece {
 // off_first = off(b_first).  The requests of the share are walked in order,
 // so no table of offsets is needed; next(units, &pc) yields the following
 // piece (units(b) returns U_b) or false after the last.  A share that ends
-// inside a request's start-up positions holds none of its tiles.
+// inside a request's start-up positions holds none of its tiles.  Once next()
+// has returned false, b and ob locate start(g+1) the same way.
 struct BalancedWalk {
   int64_t v, v_end, ob, wg;
   int32_t b, rb;
@@ -137,8 +138,10 @@ struct BalancedWalk {
     pc->slot = whole ? -1 : (int32_t)(2 * wg + (first ? 0 : 1));
     first = false;
     v = pe;
-    ob = oe;
-    b++;
+    if (pe == oe) {   // request b ends in this share; otherwise the next share starts inside it
+      ob = oe;
+      b++;
+    }
     return true;
   }
 };
@@ -152,6 +155,41 @@ MLA_HD void balanced_pieces(int64_t g, int64_t G, int32_t rb, int32_t nrb, int64
   w.init(g, G, rb, nrb, total, b_first, off_first);
   Piece pc;
   while (w.next(units, &pc)) fn(pc);
+}
+
+// Launch folding (balanced mode).  A split workgroup holds a whole CU, so a
+// plan with more groups than the device holds at once (a minimum of work
+// units above the CU count) would otherwise run in rounds, every round's
+// workgroups paying their own start-up.  Instead the launch has at most
+// resident / nrb groups, and each of its workgroups walks vg_per consecutive
+// groups of the plan in order.  The plan itself -- its groups, pieces and
+// partial slots -- is unchanged; only the launch index -> group map is.
+MLA_HD int32_t fold_factor(int64_t groups, int32_t nrb, int32_t num_splits, int32_t resident) {
+  if (num_splits > 0 || groups <= 0) return 1;
+  int64_t max_groups = resident / nrb;
+  if (max_groups < 1) max_groups = 1;
+  return groups <= max_groups ? 1 : (int32_t)((groups + max_groups - 1) / max_groups);
+}
+// Groups the folded launch covers (launch_grid pads them to whole XCD rounds).
+MLA_HD int64_t launched_groups(int64_t groups, int32_t vg_per) { return (groups + vg_per - 1) / vg_per; }
+
+// All pieces of balanced-mode groups g0 .. g1-1 for row block rb, in order:
+// fn(Piece, g) for each.  b_first / off_first locate start(g0) as for
+// BalancedWalk; where one group's share ends, its walk stands at the request
+// holding the next group's start, which seeds the next walk.
+template <class Units, class Fn>
+MLA_HD void folded_balanced_pieces(int64_t g0, int64_t g1, int64_t G, int32_t rb, int32_t nrb, int64_t total,
+                                   int32_t b_first, int64_t off_first, const Units& units, Fn&& fn) {
+  int32_t b = b_first;
+  int64_t ob = off_first;
+  for (int64_t g = g0; g < g1; g++) {
+    BalancedWalk w;
+    w.init(g, G, rb, nrb, total, b, ob);
+    Piece pc;
+    while (w.next(units, &pc)) fn(pc, g);
+    b = w.b;
+    ob = w.ob;
+  }
 }
 
 // The single piece of forced-mode group g for row block rb, or false.  U is

@@ -21,8 +21,8 @@ hipError_t mla_launch_gather(const void*, const int32_t*, const int32_t*, int32_
                              int32_t, int32_t, void*, hipStream_t) {
   return hipErrorNoDevice;
 }
-hipError_t mla_launch_plan(const int32_t*, int32_t, int32_t, int32_t, int32_t, int64_t, int32_t, int32_t*, int32_t*,
-                           hipStream_t) {
+hipError_t mla_launch_plan(const int32_t*, int32_t, int32_t, int32_t, int32_t, int64_t, int32_t, int32_t, int32_t*,
+                           int32_t*, hipStream_t) {
   return hipErrorNoDevice;
 }
 hipError_t mla_launch_append(const mla::AppendArgs*, hipStream_t) { return hipErrorNoDevice; }

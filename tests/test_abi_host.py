@@ -265,6 +265,13 @@ def test_ragged_argument_checks(L):
                                None) == mla.MLA_ERR_INVALID_VALUE      # negative token count
     assert L.mla_decode_ragged(ctypes.byref(p), fake, fake, 2, fake, fake, fake, fake, None, ws, 1,
                                None) == mla.MLA_ERR_WORKSPACE_TOO_SMALL  # every argument check passed
+    # no query token at all: the parameters are checked, nothing is enqueued
+    # and q, out, lse and the workspace may be null
+    assert L.mla_decode_ragged(ctypes.byref(p), None, fake, 0, fake, fake, fake, None, None, None, 0,
+                               None) == mla.MLA_OK
+    bad = good(page_size=16)
+    assert L.mla_decode_ragged(ctypes.byref(bad), None, fake, 0, fake, fake, fake, None, None, None, 0,
+                               None) == mla.MLA_ERR_INVALID_VALUE
 
 
 def test_ragged_algorithmic_work():

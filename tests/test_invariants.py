@@ -105,7 +105,8 @@ def test_split_count_sweep(orc, S):
     assert o.tobytes() == o2.tobytes() and l.tobytes() == l2.tobytes(), "not deterministic"
 
 
-@pytest.mark.parametrize("units", [1, 3, 17, 256, 1000])
+# above 256 / nrb groups the launch folds several plan groups into each workgroup
+@pytest.mark.parametrize("units", [1, 3, 17, 256, 1000, 4000])
 def test_balanced_grid_sweep(orc, units):
     inp = P.small(q_len=2, lens=(2, 333, 2048, 4000), heads=64, seed=48)
     ro, rl = orc.decode(inp)
@@ -139,7 +140,10 @@ def test_fp8_equals_bf16_on_dequantised_pool():
     G.compare(o1, l1, o2.astype(np.float64), l2.astype(np.float64), fp8=True, what="fp8 vs dequantised bf16")
 
 
-@pytest.mark.parametrize("mode", [dict(), dict(num_splits=5), dict(min_work_units=37)])
+# min_work_units 1000 and 3000: more groups than the CUs hold, so the plan
+# kernel runs folded (several plan groups per workgroup) as the decode does
+@pytest.mark.parametrize("mode", [dict(), dict(num_splits=5), dict(min_work_units=37), dict(min_work_units=1000),
+                                  dict(min_work_units=3000)])
 def test_device_plan_equals_host_plan(mode):
     L = np.array([0, 1, 31, 32, 33, 500, 4096, 77], dtype=np.int32)
     p = mla.make_params(len(L), 2, 128, 64, 1000, 64, 4096, mla.MLA_KV_BF16, 0.07, 1.0,

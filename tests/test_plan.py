@@ -96,6 +96,32 @@ def test_balanced_plan_covers_and_balances(seed):
     assert part.max() <= 2
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_folded_launch_walks_the_same_plan(seed):
+    """More groups than the CUs hold (min_work_units above num_cus): each
+    launched workgroup walks several consecutive plan groups, every walk
+    continuing from where the previous group's share ended -- also inside a
+    request, inside its start-up positions, or after an empty share.  The
+    pieces are the plan's own: equal to the model written from the plan's
+    definition."""
+    rng = np.random.default_rng(300 + seed)
+    B = int(rng.integers(1, 40))
+    q_len, H = int(rng.choice([1, 2, 4])), int(rng.choice([16, 64, 128]))
+    L = rng.integers(0, 3000, size=B).astype(np.int32)
+    L[rng.random(B) < 0.2] = 0
+    L[rng.random(B) < 0.2] = 1
+    cus = int(rng.choice([8, 64, 256]))
+    p = params(B, q_len, H, int(max(L.max(), 1)), min_work_units=int(rng.integers(cus + 1, 6 * cus + 2)),
+               num_cus=cus)
+    pieces, grid = mla.mla_plan_host(p, L)
+    nrb = -(-q_len * H // mla.ROWS_PER_BLOCK)
+    check_cover(p, L, pieces, grid)
+    assert sorted(map(tuple, np.asarray(pieces).tolist())) == \
+        model_balanced_plan(L, p.max_seq_len, nrb, grid // nrb, mla.PIECE_COST)
+    # listed by plan workgroup, as the device plan lists them
+    assert np.all(np.diff(np.asarray(pieces)[:, 0]) >= 0)
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_split_requests_end_in_distinct_group_shares(seed):
     """What the combine's group grid relies on (plans with fewer groups than

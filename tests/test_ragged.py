@@ -80,6 +80,14 @@ def test_offsets_past_the_query_are_ignored():
     assert np.isnan(o[5:]).all() and np.isnan(l[5:]).all()
 
 
+def test_no_query_token_in_the_batch():
+    """Every request with q_b = 0: an empty query and output, a no-op call."""
+    inp = P.small(kv="fp8", q_len=2, heads=64, page_size=32, lens=(686, 159), seed=212, k_scale=0.5)
+    rg = ragged(inp, q_lens=[0, 0])
+    o, l = run_ragged(rg)
+    assert o.shape == (0, 64, 512) and l.shape == (0, 64)
+
+
 def test_full_size_draft_extend_sampled():
     """The MTP-shaped batch with per-request lengths uniform in [1, 4], in the
     launch configuration the benchmark times, on sampled rows."""

@@ -36,7 +36,7 @@ def _draw(seed):
     k_scale = float(r.choice([0.5, 0.25, 1.5])) if kv == "fp8" else None
     mode = r.choice(["auto", "forced", "units"])
     kw = {"auto": {}, "forced": {"num_splits": int(r.integers(1, 10))},
-          "units": {"min_work_units": int(r.integers(1, 64))}}[mode]
+          "units": {"min_work_units": int(r.choice([r.integers(1, 64), r.integers(256, 3000)]))}}[mode]
     inp = P.small(kv=kv, q_len=q_len, heads=H, page_size=Pg, lens=tuple(int(x) for x in lens), seed=7000 + seed,
                   k_scale=k_scale)
     return inp, kw, r
