@@ -390,16 +390,36 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
 // per load, converted once per tile and stored to LDS as bf16: the two
 // 16-byte LDS chunks 2c and 2c+1 of the row.  A tile's 1152 chunks take
 // 4.5 loads per loader lane: the fifth only in loader waves 0 and 1.  The
-// rows of a tile are consecutive slots of one page, so chunk ci of the tile
-// is at byte 16*ci of its first row.
+// rows of a tile are consecutive slots of one page, so chunk m of row r is
+// at byte 576*r + 16*m of the tile's first row.
 template <>
 struct Stage<true> {
   static constexpr int kChunks = kTile * kRowDim / 16;   // 1152
   static constexpr int kRowChunks = kRowDim / 16;        // 36
   static constexpr int kPer = (kChunks + kLoaderThreads - 1) / kLoaderThreads;   // 5
   static_assert(kChunks % 64 == 0, "every loader wave loads whole or no chunks");
+  static_assert(kTile == 32 && kRowChunks == 36, "chunk_of assumes 16 row pairs of 36 chunks");
   u32x4_t v[kPer];
   __device__ __forceinline__ void init(int) {}
+  // The tile chunk (row r, chunk m of the row's 36) that slot q = lt + 256*i
+  // of the loader threads carries.  Each chunk becomes the two 16-byte LDS
+  // chunks 2m and 2m + 1 of row r.  The LDS takes a 16-byte write eight
+  // lanes at a time over 128 bytes of banks (measured: the bank-conflict
+  // counter of this kernel matches that model, and no other, across three
+  // store orders), so the eight chunks a group of eight lanes writes must be
+  // distinct modulo eight.  Eight lanes on consecutive chunks of one row
+  // write chunks 32 bytes apart, two to a bank.  Instead lanes 0..3 of a
+  // group take chunks 4a .. 4a+3 of row 2s and lanes 4..7 the same chunks of
+  // row 2s + 1 (group G = 9s + a, nine groups per row pair): the even row's
+  // chunks land on the even 16-byte bank slots and the odd row's on the odd
+  // ones (an odd row's swizzle flips bit 0; the 1152-byte row pitch is a
+  // whole number of bank periods), so both writes are free of conflicts.
+  __device__ __forceinline__ static void chunk_of(int q, int& r, int& m) {
+    const int G = q >> 3, k = q & 7;
+    const int s = (G * 57) >> 9;   // G / 9 for G < 144
+    r = 2 * s + (k >> 2);
+    m = 4 * (G - 9 * s) + (k & 3);
+  }
   // Called by the loader waves; lt = thread index among them.
   __device__ __forceinline__ void load(const SplitArgs& a, PageWindow& pw, int b, int ts, int tok_end) {
     const int lt = threadIdx.x - 64 * kLoaderWave0;
@@ -411,9 +431,11 @@ struct Stage<true> {
     }
 #pragma unroll
     for (int i = 0; i < kPer; i++) {
-      const int ci = lt + kLoaderThreads * i;
+      const int q = lt + kLoaderThreads * i;
+      int r, m;
+      chunk_of(q, r, m);
       u32x4_t x = {0u, 0u, 0u, 0u};
-      if (base != nullptr && ci < kChunks && ts + ci / kRowChunks < tok_end) x = *(const u32x4_t*)(base + 16 * ci);
+      if (base != nullptr && q < kChunks && ts + r < tok_end) x = *(const u32x4_t*)(base + r * kRowDim + 16 * m);
       v[i] = x;
     }
   }
@@ -421,9 +443,10 @@ struct Stage<true> {
     const int lt = threadIdx.x - 64 * kLoaderWave0;
 #pragma unroll
     for (int i = 0; i < kPer; i++) {
-      const int ci = lt + kLoaderThreads * i;
-      if (ci >= kChunks) continue;
-      const int r = ci / kRowChunks, c = 2 * (ci - r * kRowChunks);   // LDS chunks c and c + 1 of row r
+      const int q = lt + kLoaderThreads * i;
+      if (q >= kChunks) continue;
+      int r, m;
+      chunk_of(q, r, m);
       u32x4_t y0, y1;
       y0[0] = fp8x2_to_bf16x2<false>(v[i][0]);
       y0[1] = fp8x2_to_bf16x2<true>(v[i][0]);
@@ -433,8 +456,8 @@ struct Stage<true> {
       y1[1] = fp8x2_to_bf16x2<true>(v[i][2]);
       y1[2] = fp8x2_to_bf16x2<false>(v[i][3]);
       y1[3] = fp8x2_to_bf16x2<true>(v[i][3]);
-      *(__attribute__((address_space(3))) u32x4_t*)(buf + lds_off(r, c)) = y0;
-      *(__attribute__((address_space(3))) u32x4_t*)(buf + lds_off(r, c + 1)) = y1;
+      *(__attribute__((address_space(3))) u32x4_t*)(buf + lds_off(r, 2 * m)) = y0;
+      *(__attribute__((address_space(3))) u32x4_t*)(buf + lds_off(r, 2 * m + 1)) = y1;
     }
   }
 };
