@@ -254,16 +254,17 @@ def main():
     stream = torch.cuda.current_stream()
     ind = torch.from_numpy(rg.qo_indptr).to(dev) if rg is not None else None
 
-    # Every timed step records an event before and after the split kernel on the
-    # stream both kernels run on: the split kernel's duration is (start, end) of
-    # its own step, the GPU time of a whole step is (start, next start).  A
-    # ragged call is bracketed as a whole (split kernel and combine).
+    # Every timed step records events on the stream both kernels run on: before
+    # the split kernel, after it, and after the combine.  The split kernel's
+    # duration is (start, split end) of its own step, the call's (start, call
+    # end), the GPU time of a whole step (start, next start).  A ragged call is
+    # bracketed as a whole (split kernel and combine).
     ev = HipEvents()
-    events = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    events = [(ev.create(), ev.create(), ev.create()) for _ in range(args.steps)]
 
-    def step(i, e0, e1):
+    def step(i, e0, e1, e2):
         if rg is None:
-            mla.mla_decode_timed(p, qs[i % copies], pools[i % copies], bt, sl, out, lse, ws, stream, e0, e1, None)
+            mla.mla_decode_timed(p, qs[i % copies], pools[i % copies], bt, sl, out, lse, ws, stream, e0, e1, e2)
             return
         if e0 is not None:
             ev.record(e0, stream)
@@ -273,15 +274,16 @@ def main():
             ev.record(e1, stream)
 
     for i in range(args.warmup):
-        step(i, None, None)
+        step(i, None, None, None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(args.warmup + k, events[k][0], events[k][1])
+        step(args.warmup + k, *events[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    split_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in events]))
+    split_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b, _ in events]))
+    call_ms = float(np.mean([ev.elapsed_ms(a, c) for a, _, c in events])) if rg is None else split_ms
     gpu_step_ms = float(np.mean([ev.elapsed_ms(events[k][0], events[k + 1][0])
                                  for k in range(args.steps - 1)])) if args.steps > 1 else float("nan")
     for e in events:
@@ -327,7 +329,15 @@ def main():
                 "traffic": measured_traffic(w.name, whole_call=rg is not None),
                 "kernel": "mla_split_kernel" if rg is None else "mla_split_kernel + mla_combine_kernel (one call)",
                 "algorithmic_bytes_per_launch": split_bytes, "algorithmic_flops_per_launch": flops,
-                "hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4)}
+                "hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
+                # the whole decode call (split kernel, combine and the gap
+                # between them): all its algorithmic bytes, output included,
+                # over the GPU time from before the split kernel to after the
+                # combine
+                "call": {"kernels": "mla_split_kernel + mla_combine_kernel", "ms": round(call_ms, 5),
+                         "algorithmic_bytes": nbytes,
+                         "achieved": round(nbytes / (call_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+                         "frac": round(nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
     res = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -352,7 +362,7 @@ def main():
         "decode_tokens_per_s": round(q_rows / (ms_step * 1e-3), 1),
         "algorithmic_bytes": nbytes,
         "algorithmic_flops": flops,
-        "event_ms": {"split_kernel": round(split_ms, 5), "gpu_step": round(gpu_step_ms, 5),
+        "event_ms": {"split_kernel": round(split_ms, 5), "call": round(call_ms, 5), "gpu_step": round(gpu_step_ms, 5),
                      "combine_and_launch_gaps": round(gpu_step_ms - split_ms, 5)},
         "roofline": roofline,
         "path_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),

@@ -8,11 +8,10 @@
 // latent rows; all rows share the one latent KV head, so a KV tile staged
 // once in LDS serves 128 query rows.
 //
-// Split kernel, one workgroup = 4 waves = 64 query rows (one wave per SIMD,
-// so each wave may hold its 16 rows' Q fragments and O accumulators, about
-// 200 registers, with room left for the pipeline); wave w owns rows
-// 16w..16w+15 of the row block, lane l owns row l%16 throughout.  Per
-// 32-token KV tile staged in LDS:
+// Split kernel, one workgroup = 64 query rows (a row block) of one request,
+// 16 waves in three roles (below): QK wave w owns rows 16w..16w+15 of the
+// row block, lane l owns row l%16 throughout.  Per 32-token KV tile staged
+// in LDS:
 //   S^T[32 tok x 16 rows]  = K_tile[32 x 576] . Q^T[576 x 16]   (36 MFMA 16x16x32 bf16)
 //   P^T = exp2(S^T*scale*log2e - m)  (online softmax, lazily rescaled)
 //   O^T[512 x 16 rows]    += V^T[512 x 32 tok] . P^T[32 x 16]  (32 MFMA 16x16x32 bf16)
@@ -46,22 +45,22 @@ constexpr int kThreads = 256;                      // combine / gather / plan ke
 #endif
 constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
 #ifndef MLA_KA
-#define MLA_KA 6
+#define MLA_KA 3
 #endif
 #ifndef MLA_VA
 #define MLA_VA 1
 #endif
 #ifndef MLA_SC
-#define MLA_SC 4
+#define MLA_SC 2
 #endif
 #ifndef MLA_F8_KA
-#define MLA_F8_KA 8
+#define MLA_F8_KA 3
 #endif
 #ifndef MLA_F8_VA
 #define MLA_F8_VA 1
 #endif
 #ifndef MLA_F8_SC
-#define MLA_F8_SC 4
+#define MLA_F8_SC 2
 #endif
 #ifndef MLA_F8_DEFER
 #define MLA_F8_DEFER 1
@@ -69,21 +68,24 @@ constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
 constexpr int kRowsPerWave = 16 * kRowBlocksPerWave;
 static_assert(kRowBlocksPerWave == 1, "one 16-row MFMA block per wave");
 // A split workgroup runs three kinds of wave in a pipeline over the KV tiles
-// of a piece (waves are spread evenly over the four SIMDs):
-//   QK waves      (kRowGroups) S = Q.K^T for their 16 rows on tile j+1,
+// of a piece (waves are spread evenly over the four SIMDs: one QK wave, two
+// PV waves and one loader wave on each, 128 registers per wave):
+//   QK waves      (kRowGroups = 4) S = Q.K^T for their 16 rows on tile j+1,
 //                 online softmax, P (bf16) and the rows' rescale factors out
 //                 to LDS;
-//   PV waves      (kPVWaves) O = alpha*O + P.V on tile j, each for a share of
-//                 the (row group, output dims) grid;
-//   loader waves  (kLoaderWaves) tile j+3 into the LDS ring.
-// Splitting the two products over two waves gives each one registers for a
-// deep LDS read-ahead (Q and O no longer share a wave), and the softmax of
-// one wave runs while the other keeps the matrix unit busy.  A tile load can
-// stall its wave at issue for hundreds of cycles while the memory queue is
-// full; the loader waves take those stalls.
+//   PV waves      (kPVWaves = 8) O = alpha*O + P.V on tile j, each for a
+//                 share of the (row group, output dims) grid: two row groups
+//                 times 128 output dims, 64 accumulator registers;
+//   loader waves  (kLoaderWaves = 4) tile j+3 into the LDS ring.
+// Splitting the two products over different waves gives each one its
+// registers (Q and O no longer share a wave), and the softmax of one wave
+// runs while the others keep the matrix unit busy; two PV waves per SIMD
+// overlap each other's LDS reads.  A tile load can stall its wave at issue
+// for hundreds of cycles while the memory queue is full; the loader waves
+// take those stalls.
 constexpr int kRowGroups = kRowsPerBlock / kRowsPerWave;
 #ifndef MLA_PV_WAVES
-#define MLA_PV_WAVES 4
+#define MLA_PV_WAVES 8
 #endif
 constexpr int kPVWaves = MLA_PV_WAVES;
 constexpr int kQKWave0 = 0, kPVWave0 = kRowGroups, kLoaderWave0 = kRowGroups + kPVWaves;
