@@ -271,6 +271,23 @@ mla_status mla_gather_kv(const mla_decode_params* p, const void* kv_pool, const 
 mla_status mla_plan_host(const mla_decode_params* p, const int32_t* seq_lens_host, int32_t* pieces,
                          int32_t max_pieces, int32_t* n_pieces, int32_t* grid);
 
+/* Debug/test: the plan of a ragged batch (mla_decode_ragged) on the host,
+ * with the query token offsets qo_indptr_host [B+1] (taken as the kernel
+ * takes them: offsets outside [0, total_q_tokens] or running backwards
+ * give no query token, more than p->q_len tokens give p->q_len).  In
+ * balanced mode, unfolded, with at most 8 row blocks per request, the
+ * requests are planned in row-block classes: request b has n_b row blocks
+ * (rows q_b*H), the requests with n_b = n share groups of n workgroups, and
+ * each class's groups take equal shares of that class's cost positions
+ * (*class_plan_used = 1).  Otherwise, and when every request has all its
+ * row blocks, the plan is mla_plan_host()'s (*class_plan_used = 0).
+ * Pieces as for mla_plan_host(), with the first column the workgroup's
+ * number in the plan (the class plan numbers its workgroups class by class
+ * in descending n); pieces of row blocks without rows are left out. */
+mla_status mla_plan_host_ragged(const mla_decode_params* p, const int32_t* seq_lens_host,
+                                const int32_t* qo_indptr_host, int32_t total_q_tokens, int32_t* pieces,
+                                int32_t max_pieces, int32_t* n_pieces, int32_t* grid, int32_t* class_plan_used);
+
 /* Debug/test: the same plan computed on the device by the code the decode
  * kernel runs.  pieces: device int32 [grid][max_per_wg][6]; counts: device
  * int32 [grid] (pieces of each workgroup, possibly above max_per_wg, in

@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.mla_gather_kv.argtypes = [P, vp, vp, vp, ctypes.c_int32, vp, vp]
         L.mla_plan_host.restype = ctypes.c_int
         L.mla_plan_host.argtypes = [P, vp, vp, ctypes.c_int32, i32p, i32p]
+        L.mla_plan_host_ragged.restype = ctypes.c_int
+        L.mla_plan_host_ragged.argtypes = [P, vp, vp, ctypes.c_int32, vp, ctypes.c_int32, i32p, i32p, i32p]
         L.mla_plan_device.restype = ctypes.c_int
         L.mla_plan_device.argtypes = [P, vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp]
         L.mla_check_inputs_host.restype = ctypes.c_int
@@ -475,6 +477,25 @@ def mla_plan_host(p: mla_decode_params, seq_lens_host: np.ndarray) -> Tuple[np.n
                                pieces.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(n), ctypes.byref(grid)),
            "mla_plan_host")
     return pieces[:n.value], int(grid.value)
+
+
+def mla_plan_host_ragged(p: mla_decode_params, seq_lens_host: np.ndarray, qo_indptr_host: np.ndarray,
+                         total_q_tokens: int) -> Tuple[np.ndarray, int, bool]:
+    """The plan of a ragged batch: int32 rows (g, b, row_block, tile_begin, tile_end, slot), the
+    grid size, and whether the row-block class plan was used."""
+    sl = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    qi = np.ascontiguousarray(qo_indptr_host, dtype=np.int32)
+    n, grid, used = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    args = (ctypes.byref(p), sl.ctypes.data_as(ctypes.c_void_p), qi.ctypes.data_as(ctypes.c_void_p),
+            int(total_q_tokens))
+    st = lib().mla_plan_host_ragged(*args, None, 0, ctypes.byref(n), ctypes.byref(grid), ctypes.byref(used))
+    if st not in (MLA_OK, MLA_ERR_INVALID_VALUE) or (st == MLA_ERR_INVALID_VALUE and n.value == 0 and p.batch > 0):
+        _check(st, "mla_plan_host_ragged")
+    cap = max(n.value, 1)
+    pieces = np.zeros((cap, 6), dtype=np.int32)
+    _check(lib().mla_plan_host_ragged(*args, pieces.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(n),
+                                      ctypes.byref(grid), ctypes.byref(used)), "mla_plan_host_ragged")
+    return pieces[:n.value], int(grid.value), bool(used.value)
 
 
 def mla_plan_device(p: mla_decode_params, seq_lens_dev, grid: int, max_per_wg: int, stream=None):

@@ -107,11 +107,11 @@ mla_status layout_of(const mla_decode_params* p, Layout* lay) {
     mla_status s = target_units(p, &target);
     if (s != MLA_OK) return s;
   }
-  lay->groups = mla::group_count(p->batch, nrb, p->max_seq_len, p->num_splits, target);
+  lay->groups = mla::group_count(p->batch, nrb, p->max_seq_len, p->num_splits, target, p->min_work_units > 0);
   lay->wgs = lay->groups * nrb;
   lay->slots = mla::slot_count(lay->groups, nrb, p->num_splits);
-  lay->off_pos = 0;
-  lay->off_lse = align256(((size_t)p->batch + 1) * sizeof(int32_t));
+  lay->off_pos = 0;   // offsets [B+1], then the class plan's table
+  lay->off_lse = align256(((size_t)p->batch + 1 + mla::kClassTabInts) * sizeof(int32_t));
   lay->off_o = lay->off_lse + align256((size_t)lay->slots * kRowsPerBlock * sizeof(float));
   lay->total = lay->off_o + (size_t)lay->slots * kRowsPerBlock * kLatentDim * sizeof(uint16_t);
   if (mla::launch_grid(lay->groups, nrb) > 0x7fffffff) return MLA_ERR_NOT_SUPPORTED;
@@ -246,6 +246,13 @@ static mla_status decode_impl(const mla_decode_params* p, const QueryParts& qp, 
   a.p_shift = p->page_size == 64 ? 6 : 5;
   a.vg_per = mla::fold_factor(lay.groups, a.nrb, p->num_splits, di.cus);
   a.NGL = mla::launched_groups(lay.groups, a.vg_per);
+  // a ragged batch in balanced mode, unfolded, with at most kMaxClasses row
+  // blocks: the kernel plans it in row-block classes when they fit
+  a.class_tab = a.pos_off_ws + p->batch + 1;
+  a.class_plan = qp.qo_indptr != nullptr && p->num_splits == 0 && a.vg_per == 1 &&
+                 a.nrb <= mla::kMaxClasses;
+  a.class_S = (int32_t)std::min<int64_t>(lay.groups * a.nrb, di.cus);
+  a.class_C = (int32_t)std::min<int64_t>(mla::launch_grid(lay.groups, a.nrb) / mla::kXcds, di.cus / mla::kXcds);
   a.scale_log2 = (float)((double)p->softmax_scale * (double)kscale * 1.4426950408889634);
   a.out_scale = kscale;
   hipStream_t st = (hipStream_t)stream;
@@ -270,6 +277,7 @@ static mla_status decode_impl(const mla_decode_params* p, const QueryParts& qp, 
     c.max_seq_len = a.max_seq_len;
     c.num_splits = a.num_splits;
     c.NG = a.NG;
+    c.class_tab = a.class_plan ? a.class_tab : nullptr;
     if (mla_launch_combine(&c, st) != hipSuccess) return MLA_ERR_HIP;
   }
   if (ev_end != nullptr && hipEventRecord((hipEvent_t)ev_end, st) != hipSuccess) return MLA_ERR_HIP;
@@ -431,6 +439,116 @@ mla_status mla_plan_host(const mla_decode_params* p, const int32_t* seq_lens_hos
     }
     std::stable_sort(got.begin(), got.end(), [](const auto& x, const auto& y) { return x.first < y.first; });
     for (const auto& e : got) emit(e.second, e.first);
+  }
+  *n_pieces = (int32_t)n;
+  *grid = (int32_t)lay.wgs;
+  return n > max_pieces ? MLA_ERR_INVALID_VALUE : MLA_OK;
+}
+
+mla_status mla_plan_host_ragged(const mla_decode_params* p, const int32_t* seq_lens_host,
+                                const int32_t* qo_indptr_host, int32_t total_q_tokens, int32_t* pieces,
+                                int32_t max_pieces, int32_t* n_pieces, int32_t* grid, int32_t* class_plan_used) {
+  mla_status s = check_params(p);
+  if (s != MLA_OK) return s;
+  if (n_pieces == nullptr || grid == nullptr || class_plan_used == nullptr) return MLA_ERR_INVALID_VALUE;
+  if (p->batch > 0 && (seq_lens_host == nullptr || qo_indptr_host == nullptr)) return MLA_ERR_INVALID_VALUE;
+  if (max_pieces > 0 && pieces == nullptr) return MLA_ERR_INVALID_VALUE;
+  if (total_q_tokens < 0) return MLA_ERR_INVALID_VALUE;
+  Layout lay;
+  s = layout_of(p, &lay);
+  if (s != MLA_OK) return s;
+  const int32_t B = p->batch, nrb = mla::row_blocks(p->q_len, p->num_heads);
+  const int64_t NG = lay.groups;
+  // the query tokens of request b as the kernel takes them from the offsets
+  auto q_b = [&](int32_t b) -> int32_t {
+    const int32_t st = qo_indptr_host[b], en = qo_indptr_host[b + 1];
+    if (st < 0 || en < st || en > total_q_tokens) return 0;
+    return std::min(en - st, p->q_len);
+  };
+  auto units = [&](int32_t b) -> int32_t { return mla::units_of(mla::clamp_len(seq_lens_host[b], p->max_seq_len)); };
+  auto pos = [&](int32_t b) -> int64_t { return mla::positions_of(mla::clamp_len(seq_lens_host[b], p->max_seq_len)); };
+  std::vector<std::pair<int64_t, mla::Piece>> got;   // (plan workgroup, piece)
+  *class_plan_used = 0;
+  if (p->num_splits > 0) {
+    for (int64_t g = 0; g < NG; g++)
+      for (int32_t rb = 0; rb < nrb; rb++) {
+        const int32_t b = (int32_t)(g / p->num_splits);
+        mla::Piece pc;
+        if (mla::forced_piece(g, rb, nrb, p->num_splits, units(b), &pc)) got.emplace_back(g * nrb + rb, pc);
+      }
+  } else {
+    const int32_t cus = p->num_cus > 0 ? p->num_cus : 256;
+    const int32_t vg = mla::fold_factor(NG, nrb, 0, cus);
+    // the class plan's slots: the launch's, at most the CUs (as the kernel is given them)
+    const int32_t class_S = (int32_t)std::min<int64_t>(NG * nrb, cus);
+    const int32_t class_C = (int32_t)std::min<int64_t>(mla::launch_grid(NG, nrb) / mla::kXcds, cus / mla::kXcds);
+    mla::ClassPlan cp;
+    cp.ok = false;
+    if (vg == 1 && nrb <= mla::kMaxClasses) {
+      int32_t T[mla::kMaxClasses + 1] = {0};
+      for (int32_t b = 0; b < B; b++) {
+        const int32_t n = mla::row_blocks(q_b(b), p->num_heads);
+        if (n >= 1) T[n] += (int32_t)pos(b);
+      }
+      cp = mla::make_class_plan(T, nrb, class_S, class_C);
+    }
+    if (cp.ok) {
+      *class_plan_used = 1;
+      const int32_t C = class_C;
+      for (int32_t x = 0; x < mla::kXcds; x++)
+        for (int32_t sl = 0; sl < C; sl++) {
+          int32_t g = 0, rb = 0;
+          const int32_t n = mla::class_slot(cp, nrb, C, x, sl, &g, &rb);
+          if (n == 0) continue;
+          auto member = [&](int32_t b) { return mla::row_blocks(q_b(b), p->num_heads) == n; };
+          // offsets on the class's line; the request holding the group's first position
+          const int64_t v_begin = mla::wg_start(g, cp.T[n], cp.G[n]);
+          int64_t off = 0, off_first = 0;
+          int32_t b_first = 0;
+          for (int32_t b = 0; b < B; b++) {
+            if (!member(b)) continue;
+            if (off <= v_begin) {
+              b_first = b;
+              off_first = off;
+            }
+            off += pos(b);
+          }
+          auto succ = [&](int32_t b) {
+            for (b++; b < B && !member(b); b++) {
+            }
+            return b;
+          };
+          mla::BalancedWalk w;
+          w.init(g, cp.G[n], rb, n, cp.T[n], b_first, off_first, cp.base[n]);
+          mla::Piece pc;
+          while (w.next(units, &pc, succ)) got.emplace_back(cp.base[n] + (int64_t)g * n + rb, pc);
+        }
+    } else {
+      std::vector<int64_t> off((size_t)B + 1, 0);
+      for (int32_t b = 0; b < B; b++) off[b + 1] = off[b] + pos(b);
+      const int64_t total = off[(size_t)B];
+      for (int64_t g0 = 0; g0 < NG; g0 += vg) {
+        const int64_t g1 = std::min<int64_t>(g0 + vg, NG);
+        const int64_t v_begin = mla::wg_start(g0, total, NG);
+        int32_t b_first = 0;
+        for (int32_t b = 0; b < B; b++)
+          if (off[b] <= v_begin) b_first = b;
+        for (int32_t rb = 0; rb < nrb; rb++)
+          mla::folded_balanced_pieces(g0, g1, NG, rb, nrb, total, b_first, off[(size_t)b_first], units,
+                                      [&](const mla::Piece& pc, int64_t g) { got.emplace_back(g * nrb + rb, pc); });
+      }
+    }
+  }
+  std::stable_sort(got.begin(), got.end(), [](const auto& x, const auto& y) { return x.first < y.first; });
+  int64_t n = 0;
+  for (const auto& e : got) {
+    const mla::Piece& pc = e.second;
+    if ((int64_t)pc.rb * mla::kRowsPerBlock >= (int64_t)q_b(pc.b) * p->num_heads) continue;   // no rows here
+    if (n < max_pieces) {
+      int32_t* o = pieces + n * 6;
+      o[0] = (int32_t)e.first; o[1] = pc.b; o[2] = pc.rb; o[3] = pc.tile0; o[4] = pc.tile1; o[5] = pc.slot;
+    }
+    n++;
   }
   *n_pieces = (int32_t)n;
   *grid = (int32_t)lay.wgs;

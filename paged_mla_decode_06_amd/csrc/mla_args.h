@@ -26,6 +26,11 @@ struct SplitArgs {
   int32_t rope_max_pos, rope_neox;
   int32_t B, q_len, H, P, W, N, max_seq_len, nrb, R, num_splits;
   int32_t p_shift;          // log2(P)
+  // ragged batch, balanced mode: plan the requests in row-block classes
+  // when they fit (class_S workgroup slots in all, class_C per XCD);
+  // class_tab receives the plan for the combine
+  int32_t class_plan, class_S, class_C;
+  int32_t* class_tab;
   int32_t vg_per;           // plan groups walked by each launched group (balanced mode), else 1
   int64_t NG;               // groups of the plan
   int64_t NGL;              // groups of the launch: ceil(NG / vg_per)
@@ -44,6 +49,10 @@ struct CombineArgs {
   int32_t total_q;
   int32_t B, q_len, H, nrb, R, max_seq_len, num_splits;
   int64_t NG;   // groups of the plan
+  // the split kernel's row-block class plan, or null when none can apply:
+  // [0] 1 when it was used; [1+n] T_n, [10+n] G_n, [19+n] base_n (n = 0..8);
+  // pos_off_ws then holds each request's offset on its class's line
+  const int32_t* class_tab;
 };
 
 struct AppendArgs {

@@ -319,6 +319,11 @@ struct Stage<false> {
   // Called by loader wave lw; returns the number of loads it issued (0 or kLoadsPerWave).
   __device__ __forceinline__ int issue(const SplitArgs& a, lds_char* buf, PageWindow& pw, int b, int ts,
                                        int tok_end, int lw) const {
+    // wave-uniform by construction; said so, so that the tile base lands in
+    // scalar registers as the DMA instruction requires
+    b = __builtin_amdgcn_readfirstlane(b);
+    ts = __builtin_amdgcn_readfirstlane(ts);
+    tok_end = __builtin_amdgcn_readfirstlane(tok_end);
     const int wave = lw;
     if (ts >= tok_end) {
       // no valid token (a request with no token at all): zeros instead, so
@@ -934,17 +939,15 @@ __device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
   lds_barrier();   // every wave has read its rows before the next piece's tile loads land there
 }
 
-// Block-wide computation of the balanced plan's cost-position offsets
-// off[0..B] into LDS.
-// part: NT ints of LDS scratch.
-template <int NT>
-__device__ void build_pos_offsets(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t* off,
-                                   int32_t* part) {
+// Block-wide prefix sums off[0..B] of per-request cost positions pos(b)
+// into LDS.  part: NT ints of LDS scratch.
+template <int NT, class Pos>
+__device__ void build_offsets(int32_t B, const Pos& pos, int32_t* off, int32_t* part) {
   const int tid = threadIdx.x;
   const int per = (B + NT - 1) / NT;
   const int b0 = tid * per, b1 = min(B, b0 + per);
   int32_t sum = 0;
-  for (int b = b0; b < b1; b++) sum += positions_of(clamp_len(seq_lens[b], max_seq_len));
+  for (int b = b0; b < b1; b++) sum += pos(b);
   part[tid] = sum;
   __syncthreads();
   // inclusive scan of part[] (Hillis-Steele)
@@ -957,10 +960,17 @@ __device__ void build_pos_offsets(const int32_t* seq_lens, int32_t B, int32_t ma
   int32_t run = tid == 0 ? 0 : part[tid - 1];
   for (int b = b0; b < b1; b++) {
     off[b] = run;
-    run += positions_of(clamp_len(seq_lens[b], max_seq_len));
+    run += pos(b);
   }
   if (tid == NT - 1) off[B] = part[NT - 1];
   __syncthreads();
+}
+
+// The balanced plan's cost-position offsets off[0..B] (all requests).
+template <int NT>
+__device__ void build_pos_offsets(const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t* off,
+                                   int32_t* part) {
+  build_offsets<NT>(B, [&](int b) { return positions_of(clamp_len(seq_lens[b], max_seq_len)); }, off, part);
 }
 
 // Balanced mode with B <= 64 * kWaveScanPer: the same offsets computed by one
@@ -1027,29 +1037,147 @@ __device__ __forceinline__ int32_t find_request(const int32_t* off, int32_t B, i
   return lo;
 }
 
+// Row blocks of request b of a ragged batch: its class in the class plan.
+__device__ __forceinline__ int32_t class_of(const SplitArgs& a, int32_t b) {
+  return row_blocks(q_extent<true>(a, b).qb, a.H);
+}
+// The same where b is wave-uniform (the walks): the result is too, and is
+// said so, so that the walk's state stays in scalar registers.
+__device__ __forceinline__ int32_t class_of_uniform(const SplitArgs& a, int32_t b) {
+  return __builtin_amdgcn_readfirstlane(class_of(a, b));
+}
+
+// Where a workgroup's walk starts.  Uniform plan: the first plan group grp
+// and its row block rb, with b_first / off_first locating the group's share
+// on the line of all requests (cls = 0).  Class plan: group grp of class
+// cls (cls_G groups, dense base cls_base), on the line of that class's
+// requests only.
+struct WalkStart {
+  int64_t grp;
+  int32_t rb, total, b_first, off_first;
+  int32_t cls, cls_G, cls_base;
+};
+
+// Class plan of a ragged batch (every thread of the workgroup): the class
+// totals, the plan, this workgroup's group, and where its share starts.
+// Returns false when the class plan does not apply (the uniform plan
+// does); *none is set when the class plan leaves this workgroup without a
+// group.  Block 0 publishes the plan, and the first workgroup of each class
+// its requests' offsets, for the combine.
+__device__ __forceinline__ bool class_start(const SplitArgs& a, char* smem, WalkStart* ws, bool* none) {
+  constexpr int NT = kSplitThreads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* red = (int32_t*)smem;   // [NT / 64][kMaxClasses]
+  int32_t t[kMaxClasses + 1];
+#pragma unroll
+  for (int k = 0; k <= kMaxClasses; k++) t[k] = 0;
+  for (int b = tid; b < a.B; b += NT) {
+    const int32_t nb = class_of(a, b);
+    const int32_t p = positions_of(clamp_len(a.seq_lens[b], a.max_seq_len));
+#pragma unroll
+    for (int k = 1; k <= kMaxClasses; k++) t[k] += nb == k ? p : 0;
+  }
+#pragma unroll
+  for (int k = 1; k <= kMaxClasses; k++) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) t[k] += __shfl_xor(t[k], d);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 1; k <= kMaxClasses; k++) red[wave * kMaxClasses + k - 1] = t[k];
+  }
+  __syncthreads();
+  int32_t T[kMaxClasses + 1];
+  T[0] = 0;
+#pragma unroll
+  for (int k = 1; k <= kMaxClasses; k++) {
+    int32_t sum = 0;
+    for (int w = 0; w < NT / 64; w++) sum += red[w * kMaxClasses + k - 1];
+    T[k] = __builtin_amdgcn_readfirstlane(sum);
+  }
+  __syncthreads();   // red is overwritten below
+  const ClassPlan cp = make_class_plan(T, a.nrb, a.class_S, a.class_C);
+  if (blockIdx.x == 0 && tid == 0) {
+    a.class_tab[0] = cp.ok ? 1 : 0;
+#pragma unroll
+    for (int n = 0; n <= kMaxClasses; n++) {
+      a.class_tab[kTabT + n] = cp.T[n];
+      a.class_tab[kTabG + n] = cp.G[n];
+      a.class_tab[kTabBase + n] = cp.base[n];
+    }
+  }
+  *none = false;
+  if (!cp.ok) return false;
+  int32_t g = 0, rb = 0;
+  const int32_t n = class_slot(cp, a.nrb, a.class_C, (int32_t)(blockIdx.x % kXcds), (int32_t)(blockIdx.x / kXcds),
+                               &g, &rb);
+  if (n == 0) {
+    *none = true;
+    return true;
+  }
+  int32_t total = 0, G = 0, base = 0;
+#pragma unroll
+  for (int k = 1; k <= kMaxClasses; k++) {
+    if (n == k) {
+      total = cp.T[k];
+      G = cp.G[k];
+      base = cp.base[k];
+    }
+  }
+  // offsets on the class's line: requests of other classes take no positions
+  int32_t* off = (int32_t*)smem;
+  build_offsets<NT>(
+      a.B, [&](int b) { return class_of(a, b) == n ? positions_of(clamp_len(a.seq_lens[b], a.max_seq_len)) : 0; },
+      off, off + kMaxBatch + 1);
+  const int64_t v_begin = wg_start(g, total, G);
+  ws->grp = g;
+  ws->rb = rb;
+  ws->total = total;
+  ws->b_first = __builtin_amdgcn_readfirstlane(find_request(off, a.B, v_begin));
+  ws->off_first = __builtin_amdgcn_readfirstlane(off[ws->b_first]);
+  ws->cls = n;
+  ws->cls_G = G;
+  ws->cls_base = base;
+  if (g == 0 && rb == 0)
+    for (int b = tid; b < a.B; b += NT)
+      if (class_of(a, b) == n) a.pos_off_ws[b] = off[b];
+  __syncthreads();   // every wave has read the offsets before tiles land there
+  return true;
+}
+
 // Every wave of a workgroup walks the same pieces: the loader waves fill the
 // tile ring, the compute waves consume it; their barriers pair up one to one.
-// grp: the first plan group of the launched group (forced mode: its only one).
+// ws.grp: the first plan group of the launched group (forced mode: its only one).
 template <bool FP8, bool RAGGED, class PieceFn>
-__device__ __forceinline__ void for_each_piece(const SplitArgs& a, int64_t grp, int32_t rb, int32_t total,
-                                               int32_t b_first, int32_t off_first, PieceFn&& fn_all) {
+__device__ __forceinline__ void for_each_piece(const SplitArgs& a, const WalkStart& ws, PieceFn&& fn_all) {
   // A ragged batch's request with fewer query rows than this row block's
   // first has nothing here: every wave of the workgroup skips the piece.
   auto fn = [&](const Piece& pc) {
     if (RAGGED && pc.rb * kRowsPerBlock >= q_extent<RAGGED>(a, pc.b).qb * a.H) return;
     fn_all(pc);
   };
+  auto units = [&](int32_t b) -> int32_t { return units_of(clamp_len(a.seq_lens[b], a.max_seq_len)); };
   if (a.num_splits > 0) {
-    const int32_t b = (int32_t)(grp / a.num_splits);
-    const int32_t U = units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
+    const int32_t b = (int32_t)(ws.grp / a.num_splits);
     Piece pc;
-    if (forced_piece(grp, rb, a.nrb, a.num_splits, U, &pc)) fn(pc);
+    if (forced_piece(ws.grp, ws.rb, a.nrb, a.num_splits, units(b), &pc)) fn(pc);
     return;
   }
-  auto units = [&](int32_t b) -> int32_t { return units_of(clamp_len(a.seq_lens[b], a.max_seq_len)); };
-  const int64_t g1 = min(grp + a.vg_per, a.NG);
-  folded_balanced_pieces(grp, g1, a.NG, rb, a.nrb, total, b_first, off_first, units,
-                         [&](const Piece& pc, int64_t) { fn(pc); });
+  // Balanced: the uniform plan's groups grp .. grp+vg_per-1 on the line of
+  // all requests, or the class plan's group grp on the line of its class
+  // (after request b comes the next request of the class).  One walk for
+  // both, so that the piece body is emitted once more only.
+  const bool by_class = RAGGED && ws.cls > 0;
+  auto succ = [&](int32_t b) {
+    if (!by_class) return b + 1;
+    for (b++; b < a.B && class_of_uniform(a, b) != ws.cls; b++) {
+    }
+    return b;
+  };
+  const int64_t G = by_class ? (int64_t)ws.cls_G : a.NG;
+  const int64_t g1 = by_class ? ws.grp + 1 : min(ws.grp + a.vg_per, a.NG);
+  folded_balanced_pieces(ws.grp, g1, G, ws.rb, by_class ? ws.cls : a.nrb, ws.total, ws.b_first, ws.off_first, units,
+                         [&](const Piece& pc, int64_t) { fn(pc); }, succ, by_class ? (int64_t)ws.cls_base : 0);
 }
 
 // RAGGED: per-request query lengths from a.qo_indptr (a separate
@@ -1059,9 +1187,20 @@ __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a
   extern __shared__ __attribute__((aligned(16))) char smem[];
   lds_char* tiles = (lds_char*)smem;
   int64_t lgrp;
-  int32_t rb;
-  group_of_block(blockIdx.x, a.nrb, &lgrp, &rb);
-  const int64_t grp = lgrp * a.vg_per;   // the first plan group this workgroup walks
+  WalkStart ws;
+  group_of_block(blockIdx.x, a.nrb, &lgrp, &ws.rb);
+  ws.grp = lgrp * a.vg_per;   // the first plan group this workgroup walks
+  ws.total = ws.b_first = ws.off_first = 0;
+  ws.cls = ws.cls_G = ws.cls_base = 0;
+  // A ragged batch in balanced mode: the row-block class plan when it applies.
+  bool planned = false;
+  if constexpr (RAGGED) {
+    if (a.class_plan) {
+      bool none = false;
+      planned = class_start(a, smem, &ws, &none);
+      if (none) return;
+    }
+  }
   // Balanced mode: the cost-position offsets of all requests, of which this workgroup
   // keeps only where its share starts; block 0 publishes them for the
   // combine.  Up to 64 * kWaveScanPer requests every wave computes them on its
@@ -1069,46 +1208,45 @@ __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a
   // (before any tile is loaded).  Every LDS byte a wave reads later is written
   // first in the pipeline (tiles by loads or zero fills), so nothing is
   // cleared here.
-  int32_t total = 0, b_first = 0, off_first = 0;
-  if (a.num_splits == 0) {
+  if (!planned && a.num_splits == 0) {
     if (a.B <= 64 * kWaveScanPer) {
-      const ShareStart st = wave_share_start(a, grp, blockIdx.x == 0 && threadIdx.x < 64);
-      total = __builtin_amdgcn_readfirstlane(st.total);
-      b_first = __builtin_amdgcn_readfirstlane(st.b_first);
-      off_first = __builtin_amdgcn_readfirstlane(st.off_first);
+      const ShareStart st = wave_share_start(a, ws.grp, blockIdx.x == 0 && threadIdx.x < 64);
+      ws.total = __builtin_amdgcn_readfirstlane(st.total);
+      ws.b_first = __builtin_amdgcn_readfirstlane(st.b_first);
+      ws.off_first = __builtin_amdgcn_readfirstlane(st.off_first);
     } else {
       int32_t* off = (int32_t*)smem;
       build_pos_offsets<kSplitThreads>(a.seq_lens, a.B, a.max_seq_len, off, off + kMaxBatch + 1);
       if (blockIdx.x == 0)
         for (int b = threadIdx.x; b <= a.B; b += kSplitThreads) a.pos_off_ws[b] = off[b];
-      total = __builtin_amdgcn_readfirstlane(off[a.B]);
-      const int64_t v_begin = wg_start(grp, total, a.NG);
-      if (v_begin < total) {
-        b_first = __builtin_amdgcn_readfirstlane(find_request(off, a.B, v_begin));
-        off_first = __builtin_amdgcn_readfirstlane(off[b_first]);
+      ws.total = __builtin_amdgcn_readfirstlane(off[a.B]);
+      const int64_t v_begin = wg_start(ws.grp, ws.total, a.NG);
+      if (v_begin < ws.total) {
+        ws.b_first = __builtin_amdgcn_readfirstlane(find_request(off, a.B, v_begin));
+        ws.off_first = __builtin_amdgcn_readfirstlane(off[ws.b_first]);
       }
       __syncthreads();   // every wave has read the offsets before tiles land there
     }
   }
-  if (lgrp >= a.NGL) return;
+  if (!planned && lgrp >= a.NGL) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave >= kLoaderWave0) {
     if (MLA_PRIO_LD) __builtin_amdgcn_s_setprio(MLA_PRIO_LD);
     const int lw = wave - kLoaderWave0;
     Stage<FP8> stg;
     stg.init(lw);
-    for_each_piece<FP8, RAGGED>(a, grp, rb, total, b_first, off_first,
+    for_each_piece<FP8, RAGGED>(a, ws,
                                 [&](const Piece& pc) { load_piece<FP8>(a, tiles, stg, pc, lw); });
   } else if (wave >= kPVWave0) {
     LaneOffsets lo_;
     lo_.init();
-    for_each_piece<FP8, RAGGED>(a, grp, rb, total, b_first, off_first,
+    for_each_piece<FP8, RAGGED>(a, ws,
                                 [&](const Piece& pc) { pv_piece<FP8, RAGGED>(a, tiles, lo_, pc, wave - kPVWave0); });
   } else {
     if (MLA_PRIO_QK) __builtin_amdgcn_s_setprio(MLA_PRIO_QK);
     LaneOffsets lo_;
     lo_.init();
-    for_each_piece<FP8, RAGGED>(a, grp, rb, total, b_first, off_first,
+    for_each_piece<FP8, RAGGED>(a, ws,
                                 [&](const Piece& pc) { qk_piece<FP8, RAGGED>(a, tiles, lo_, pc, wave - kQKWave0); });
   }
 }
@@ -1149,6 +1287,8 @@ __global__ __launch_bounds__(kThreads, kWaves == 1 ? 8 : 4) void mla_combine_ker
   const int row_in_blk = (int)(blockIdx.x - blk * chunks) * kRowsPerWg + (kWaves == 1 ? wave : 0);
   int32_t b, rb;
   int64_t g0, g1, first_pos = 0, total = 0;
+  int64_t NGc = a.NG, slot_base = 0;   // the plan's groups (of the request's class) and its first slot
+  int32_t nrbc = a.nrb;                // workgroups per group
   if constexpr (kByGroup) {
     // every wave of the workgroup takes part before any returns
     const int64_t g = blk / a.nrb;
@@ -1187,6 +1327,19 @@ __global__ __launch_bounds__(kThreads, kWaves == 1 ? 8 : 4) void mla_combine_ker
     if (Sp <= 1) return;
     g0 = (int64_t)b * a.num_splits;
     g1 = g0 + Sp - 1;
+  } else if (a.class_tab != nullptr && a.class_tab[0] == 1) {
+    // the row-block class plan of a ragged batch: the request's class n is
+    // its row-block count, its offset is on the line of that class
+    const int32_t n = row_blocks(qe.qb, a.H);
+    total = a.class_tab[kTabT + n];
+    NGc = a.class_tab[kTabG + n];
+    nrbc = n;
+    slot_base = 2 * (int64_t)a.class_tab[kTabBase + n];
+    first_pos = a.pos_off_ws[b];
+    const int32_t U = units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
+    g0 = first_group(first_pos, total, NGc);
+    g1 = last_group(first_pos, U, total, NGc);
+    if (g0 == g1) return;
   } else {
     // the request's cost positions give its tile count too (positions_of),
     // so the three offsets load together and seq_lens is not read
@@ -1199,8 +1352,8 @@ __global__ __launch_bounds__(kThreads, kWaves == 1 ? 8 : 4) void mla_combine_ker
   }
   auto slot_of = [&](int64_t g) -> int64_t {
     if (a.num_splits > 0) return g * a.nrb + rb;
-    if (wg_start(g, total, a.NG) == wg_start(g + 1, total, a.NG)) return -1;   // an empty group
-    return balanced_slot(g, g0, first_pos, total, a.NG, rb, a.nrb);
+    if (wg_start(g, total, NGc) == wg_start(g + 1, total, NGc)) return -1;   // an empty group
+    return slot_base + balanced_slot(g, g0, first_pos, total, NGc, rb, nrbc);
   };
   const int64_t n = g1 - g0 + 1;
   // Lane l handles piece c0 + l of each chunk of 64: its slot, its LSE and
@@ -1409,7 +1562,9 @@ hipError_t mla_launch_combine(const mla::CombineArgs* a, hipStream_t stream) {
   // a workgroup per row when requests are split into many pieces on average
   const bool wide = a->num_splits > 0 ? a->num_splits >= 8 : a->NG >= 4 * (int64_t)a->B;
   // the grid over groups when they are fewer than the requests
-  const bool by_group = !wide && a->num_splits == 0 && a->NG < a->B && a->B <= mla::kByGroupMaxB;
+  // (not with a class plan, whose groups are per class)
+  const bool by_group = !wide && a->num_splits == 0 && a->NG < a->B && a->B <= mla::kByGroupMaxB &&
+                        a->class_tab == nullptr;
   const int rows_per_wg = wide ? mla::CombineShape<4>::kRowsPerWg : mla::CombineShape<1>::kRowsPerWg;
   const int64_t units = by_group ? a->NG : (int64_t)a->B;
   const int64_t blocks = units * a->nrb * (mla::kRowsPerBlock / rows_per_wg);

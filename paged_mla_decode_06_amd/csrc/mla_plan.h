@@ -68,13 +68,25 @@ MLA_HD int64_t wg_start(int64_t g, int64_t total, int64_t G) { return g * total 
 // The group whose share holds position v (0 <= v < total): the largest g with start(g) <= v.
 MLA_HD int64_t wg_of_pos(int64_t v, int64_t total, int64_t G) { return ((v + 1) * G - 1) / total; }
 
-// Groups of the plan.  Balanced: about target workgroups, never more groups
-// than B * units_of(max_seq_len) (which bounds the true unit count).
-MLA_HD int64_t group_count(int32_t B, int32_t nrb, int32_t max_seq_len, int32_t num_splits, int32_t target) {
+// Groups of the plan, never more than B * units_of(max_seq_len) (which
+// bounds the true unit count).  Balanced with at_least (a minimum number of
+// work units): at least target workgroups.  Balanced otherwise (target =
+// the CU count): as many groups as the CUs hold in one round with whole
+// groups on each XCD (a group's workgroups share an XCD, and an XCD has
+// target / 8 CUs), so that no workgroup waits for a second round.
+MLA_HD int64_t group_count(int32_t B, int32_t nrb, int32_t max_seq_len, int32_t num_splits, int32_t target,
+                           bool at_least) {
   if (B <= 0) return 0;
   if (num_splits > 0) return (int64_t)B * num_splits;
   const int64_t ub = (int64_t)B * units_of(max_seq_len);
-  int64_t t = ((int64_t)(target < 1 ? 1 : target) + nrb - 1) / nrb;
+  if (target < 1) target = 1;
+  int64_t t;
+  if (at_least)
+    t = ((int64_t)target + nrb - 1) / nrb;
+  else if (target / kXcds >= nrb)
+    t = (int64_t)kXcds * ((target / kXcds) / nrb);
+  else
+    t = target / nrb > 0 ? target / nrb : 1;
   return ub < t ? ub : t;
 }
 // Workgroups launched: groups padded to a multiple of the XCD count, nrb each.
@@ -110,17 +122,23 @@ struct BalancedWalk {
   int32_t b, rb;
   bool first;
   MLA_HD void init(int64_t g, int64_t G, int32_t rb_, int32_t nrb, int64_t total, int32_t b_first,
-                   int64_t off_first) {
+                   int64_t off_first, int64_t wg_base = 0) {
     v = wg_start(g, total, G);
     v_end = wg_start(g + 1, total, G);
     ob = off_first;
-    wg = g * nrb + rb_;
+    wg = wg_base + g * nrb + rb_;
     b = b_first;
     rb = rb_;
     first = true;
   }
+  // succ(b): the request after b on the line of positions (b + 1 unless the
+  // line holds only some of the requests)
   template <class Units>
   MLA_HD bool next(const Units& units, Piece* pc) {
+    return next(units, pc, [](int32_t b) { return b + 1; });
+  }
+  template <class Units, class Succ>
+  MLA_HD bool next(const Units& units, Piece* pc, const Succ& succ) {
     if (v >= v_end) return false;
     const int32_t U = units(b);
     const int64_t oe = ob + kPieceCost + U;      // end of request b's positions
@@ -140,7 +158,7 @@ struct BalancedWalk {
     v = pe;
     if (pe == oe) {   // request b ends in this share; otherwise the next share starts inside it
       ob = oe;
-      b++;
+      b = succ(b);
     }
     return true;
   }
@@ -177,19 +195,155 @@ MLA_HD int64_t launched_groups(int64_t groups, int32_t vg_per) { return (groups 
 // fn(Piece, g) for each.  b_first / off_first locate start(g0) as for
 // BalancedWalk; where one group's share ends, its walk stands at the request
 // holding the next group's start, which seeds the next walk.
-template <class Units, class Fn>
+// succ and wg_base as for BalancedWalk (defaults: every request, in order,
+// and workgroups numbered from 0).
+template <class Units, class Fn, class Succ>
 MLA_HD void folded_balanced_pieces(int64_t g0, int64_t g1, int64_t G, int32_t rb, int32_t nrb, int64_t total,
-                                   int32_t b_first, int64_t off_first, const Units& units, Fn&& fn) {
+                                   int32_t b_first, int64_t off_first, const Units& units, Fn&& fn,
+                                   const Succ& succ, int64_t wg_base = 0) {
   int32_t b = b_first;
   int64_t ob = off_first;
   for (int64_t g = g0; g < g1; g++) {
     BalancedWalk w;
-    w.init(g, G, rb, nrb, total, b, ob);
+    w.init(g, G, rb, nrb, total, b, ob, wg_base);
     Piece pc;
-    while (w.next(units, &pc)) fn(pc, g);
+    while (w.next(units, &pc, succ)) fn(pc, g);
     b = w.b;
     ob = w.ob;
   }
+}
+template <class Units, class Fn>
+MLA_HD void folded_balanced_pieces(int64_t g0, int64_t g1, int64_t G, int32_t rb, int32_t nrb, int64_t total,
+                                   int32_t b_first, int64_t off_first, const Units& units, Fn&& fn) {
+  folded_balanced_pieces(g0, g1, G, rb, nrb, total, b_first, off_first, units, fn, [](int32_t b) { return b + 1; });
+}
+
+// ---- Row-block classes: the balanced plan of a ragged batch.
+//
+// With per-request query lengths q_b, request b has n_b = row_blocks(q_b, H)
+// row blocks, between 0 and nrb.  A uniform plan gives every group nrb
+// workgroups, so the workgroups of the row blocks a request lacks sit idle
+// for its pieces.  The class plan gives the requests of each class n (those
+// with n_b = n) groups of n workgroups: class n's requests, in batch order,
+// are laid on a line of their own cost positions (total T_n), cut into G_n
+// equal shares as in the uniform plan.  The groups' workgroups are numbered
+// densely, class by class in descending n (class n starts at base_n), and a
+// partial piece of group g, row block rb of class n goes to slot
+// 2*(base_n + g*n + rb) (first piece of the group) or that plus one (last).
+//
+// Placement: the launch has 8 XCDs of C workgroup slots each (workgroup i
+// runs on XCD i mod 8 as slot i / 8).  Groups are placed whole on one XCD,
+// so that a tile's second and later reads hit that XCD's L2: classes in
+// descending n, groups in order, each into the current XCD while it has
+// room, else into the next (next fit).  G_n is first set in proportion to
+// the class's work n*T_n (at least one group per class with work) within
+// S slots in all; then, while next fit cannot place every group, the class
+// with the most slots gives up a group.  (Striping each class's groups over
+// all XCDs, so that every XCD carries the same mix of classes, measured 2 %
+// slower on a draft-extend batch.)
+constexpr int kMaxClasses = 8;   // the class plan is used for nrb <= 8
+// The plan as published for the combine: [0] 1 when the class plan was
+// used, [1 + n] T_n, [10 + n] G_n, [19 + n] base_n for n = 0..8.
+constexpr int kClassTabInts = 32;
+constexpr int kTabT = 1, kTabG = 10, kTabBase = 19;
+
+struct ClassPlan {
+  int32_t T[kMaxClasses + 1];      // cost positions of class n (index n = 1..nrb)
+  int32_t G[kMaxClasses + 1];      // groups of class n
+  int32_t base[kMaxClasses + 1];   // dense workgroup number of class n's first workgroup
+  bool ok;                         // false: the uniform plan applies
+};
+
+// Whether next fit places G_n groups of n slots for every class, 8 XCDs of C slots.
+MLA_HD bool class_fit(const int32_t* G, int32_t nrb, int32_t C) {
+  int32_t x = 0, u = 0;
+  for (int n = kMaxClasses; n >= 1; n--) {
+    if (n > nrb) continue;
+    int32_t left = G[n];
+    while (left > 0) {
+      const int32_t fit = (C - u) / n;
+      if (fit <= 0) {
+        if (++x >= kXcds) return false;
+        u = 0;
+        continue;
+      }
+      const int32_t k = fit < left ? fit : left;
+      u += k * n;
+      left -= k;
+    }
+  }
+  return true;
+}
+
+// The class plan for class totals T[1..nrb] within S workgroup slots, C per
+// XCD.  Not ok when nrb > kMaxClasses, when no class has work, when every
+// request has all nrb row blocks (the uniform plan is then the same plan),
+// or when the classes do not fit.
+MLA_HD ClassPlan make_class_plan(const int32_t* T, int32_t nrb, int32_t S, int32_t C) {
+  ClassPlan cp;
+  cp.ok = false;
+  for (int n = 0; n <= kMaxClasses; n++) {
+    cp.T[n] = n >= 1 && n <= nrb ? T[n] : 0;
+    cp.G[n] = 0;
+    cp.base[n] = 0;
+  }
+  if (nrb > kMaxClasses) return cp;
+  int64_t work = 0;
+  int32_t need = 0;
+  bool other = false;   // work in a class below nrb
+  for (int n = 1; n <= kMaxClasses; n++) {
+    if (cp.T[n] <= 0) continue;
+    work += (int64_t)n * cp.T[n];
+    need += n;
+    other = other || n < nrb;
+  }
+  if (work == 0 || !other || need > S) return cp;
+  const int64_t R = S - need;
+  for (int n = 1; n <= kMaxClasses; n++)
+    cp.G[n] = cp.T[n] > 0 ? 1 + (int32_t)(R * cp.T[n] / work) : 0;
+  while (!class_fit(cp.G, nrb, C)) {
+    int m = 0;   // the class with the most slots that can give up a group
+    for (int n = 1; n <= kMaxClasses; n++)
+      if (cp.G[n] >= 2 && (m == 0 || cp.G[n] * n >= cp.G[m] * m)) m = n;
+    if (m == 0) return cp;
+    cp.G[m]--;
+  }
+  int32_t dense = 0;
+  for (int n = kMaxClasses; n >= 1; n--) {
+    cp.base[n] = dense;
+    dense += cp.G[n] * n;
+  }
+  cp.ok = true;
+  return cp;
+}
+
+// The group at slot s of XCD x under next fit: returns its class n (0 if the
+// slot holds none) and sets *g and *rb.
+MLA_HD int32_t class_slot(const ClassPlan& cp, int32_t nrb, int32_t C, int32_t x_me, int32_t s_me, int32_t* g,
+                          int32_t* rb) {
+  int32_t x = 0, u = 0;
+  for (int n = kMaxClasses; n >= 1; n--) {
+    if (n > nrb) continue;
+    int32_t left = cp.G[n], placed = 0;
+    while (left > 0) {
+      const int32_t fit = (C - u) / n;
+      if (fit <= 0) {
+        if (++x >= kXcds) return 0;
+        u = 0;
+        continue;
+      }
+      const int32_t k = fit < left ? fit : left;
+      if (x == x_me && s_me >= u && s_me < u + k * n) {
+        *g = placed + (s_me - u) / n;
+        *rb = (s_me - u) % n;
+        return n;
+      }
+      u += k * n;
+      placed += k;
+      left -= k;
+    }
+  }
+  return 0;
 }
 
 // The single piece of forced-mode group g for row block rb, or false.  U is

@@ -112,21 +112,22 @@ def test_empty_batch_is_a_noop(L):
 
 
 def test_workspace_size_formula():
-    # balanced: groups = min(ceil(CUs / nrb), B*units(max)); slots = 2 * groups * nrb;
-    # per slot ROWS_PER_BLOCK rows x (512 bf16 + 1 fp32 lse)
+    # balanced: groups = min(whole groups the 8 XCDs of CUs/8 CUs hold, B*units(max));
+    # slots = 2 * groups * nrb; per slot ROWS_PER_BLOCK rows x (512 bf16 + 1 fp32 lse);
+    # the request offsets [B+1] and the 32-int class table first
     a256 = lambda x: (x + 255) // 256 * 256
     R = mla.ROWS_PER_BLOCK
     for heads, q_len in [(128, 1), (128, 4), (16, 1), (64, 3)]:
         p = good(batch=64, num_heads=heads, q_len=q_len, max_seq_len=4096, block_table_stride=64, num_cus=256)
         nrb = -(-q_len * heads // R)
-        groups = min(-(-256 // nrb), 64 * 128)
+        groups = min(8 * (32 // nrb), 64 * 128)
         slots = 2 * groups * nrb
-        expect = a256(65 * 4) + a256(slots * R * 4) + slots * R * 512 * 2
+        expect = a256((65 + 32) * 4) + a256(slots * R * 4) + slots * R * 512 * 2
         assert mla.mla_decode_workspace_size(p) == expect, (heads, q_len)
     # forced splits: groups = B*S, slots = groups * nrb
     p = good(batch=3, num_heads=128, q_len=2, num_splits=5, num_cus=0)
     slots = 3 * 5 * -(-2 * 128 // R)
-    assert mla.mla_decode_workspace_size(p) == a256(4 * 4) + a256(slots * R * 4) + slots * R * 512 * 2
+    assert mla.mla_decode_workspace_size(p) == a256((4 + 32) * 4) + a256(slots * R * 4) + slots * R * 512 * 2
 
 
 def test_check_inputs_host():

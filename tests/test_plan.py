@@ -194,3 +194,144 @@ def test_long_context_workload_plan():
     pieces, grid = mla.mla_plan_host(p, L)
     assert grid >= 512
     check_cover(p, L, pieces, grid)
+
+
+# ---- ragged batches: the row-block class plan
+
+def model_class_plan(T, nrb, S, C):
+    """The class plan from its definition: at least one group per class with
+    work, the rest of the S slots in proportion to each class's work n*T_n
+    (groups G_n = 1 + floor(R*T_n/work)); while next fit (classes in
+    descending n, 8 XCDs of C slots, a group whole on one XCD) cannot place
+    every group, the class with the most slots (the larger n on a tie) gives
+    up one.  None where the uniform plan applies."""
+    if nrb > 8:
+        return None
+    cls = [n for n in range(1, nrb + 1) if T[n] > 0]
+    work = sum(n * T[n] for n in cls)
+    if work == 0 or not any(n < nrb for n in cls) or sum(cls) > S:
+        return None
+    R = S - sum(cls)
+    G = {n: (1 + R * T[n] // work if n in cls else 0) for n in range(1, 9)}
+
+    def fits():
+        bins = [0] * 8
+        x = 0
+        for n in range(8, 0, -1):
+            for _ in range(G[n]):
+                while x < 8 and bins[x] + n > C:
+                    x += 1
+                if x == 8:
+                    return False
+                bins[x] += n
+        return True
+
+    while not fits():
+        m = max((n for n in G if G[n] >= 2), key=lambda n: (G[n] * n, n), default=None)
+        if m is None:
+            return None
+        G[m] -= 1
+    base, dense = {}, 0
+    for n in range(8, 0, -1):
+        base[n] = dense
+        dense += G[n] * n
+    return G, base
+
+
+def _ragged_case(seed):
+    rng = np.random.default_rng(500 + seed)
+    B = int(rng.integers(1, 60))
+    H = int(rng.choice([16, 32, 64, 128] if seed % 4 == 0 else [64, 128]))
+    q_max = int(rng.integers(1, 5) if seed % 4 == 0 else rng.integers(2, 5))
+    while q_max * H > 512:     # at most 8 row blocks, so that the class plan may apply
+        q_max -= 1
+    L = rng.integers(0, 3000, size=B).astype(np.int32)
+    ql = rng.integers(0, q_max + 1, size=B)
+    if seed % 3 == 0:
+        ql[:] = q_max             # every request with all its row blocks: the uniform plan
+    ind = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    cus = int(rng.choice([64, 256]))
+    p = params(B, q_max, H, int(max(L.max(), 1)), num_cus=cus)
+    return p, L, ql, ind, H, q_max
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_ragged_class_plan_is_its_definition(seed):
+    """The host mirror of the ragged plan against the plan written out from
+    its definition: every request's row blocks with rows covered exactly
+    once, and with the class plan, each class's pieces those of a balanced
+    plan over that class's requests alone, renumbered into the dense slots."""
+    p, L, ql, ind, H, q_max = _ragged_case(seed)
+    pieces, grid, used = mla.mla_plan_host_ragged(p, L, ind, int(ind[-1]))
+    nrb = -(-q_max * H // mla.ROWS_PER_BLOCK)
+    NG = grid // nrb
+    nb = np.array([-(-int(q) * H // mla.ROWS_PER_BLOCK) for q in ql])
+    c = mla.PIECE_COST
+    U = np.maximum(1, -(-np.clip(L, 0, p.max_seq_len) // mla.TILE))
+    # coverage: (b, rb) for rb < n_b tiled exactly once, nothing for the rest
+    cover = {}
+    for g, b, rb, t0, t1, slot in pieces:
+        assert rb < nb[b]
+        cover.setdefault((b, rb), []).append((t0, t1, slot))
+    assert set(cover) == {(b, rb) for b in range(len(L)) for rb in range(nb[b])}
+    slots = [s for _, _, _, _, _, s in pieces if s >= 0]
+    assert len(slots) == len(set(slots)) and all(s < 2 * NG * nrb for s in slots)
+    for (b, rb), lst in cover.items():
+        lst.sort()
+        assert lst[0][0] == 0 and lst[-1][1] == U[b]
+        assert all(a[1] == n[0] for a, n in zip(lst, lst[1:]))
+        assert (len(lst) == 1) == (lst[0][2] == -1)
+    T = {n: int(sum(c + U[b] for b in range(len(L)) if nb[b] == n)) for n in range(0, 9)}
+    model = model_class_plan(T, nrb, min(NG * nrb, p.num_cus), min(-(-NG // 8) * nrb, p.num_cus // 8))
+    assert used == (model is not None)
+    if model is None:
+        if (nb == nrb).all():   # the uniform plan: mla_plan_host's
+            ref, g2 = mla.mla_plan_host(p, L)
+            assert g2 == grid and np.array_equal(np.asarray(pieces), ref)
+        return
+    G, base = model
+    want = []
+    for n in range(1, 9):
+        members = [b for b in range(len(L)) if nb[b] == n]
+        if not members:
+            continue
+        for wg, bl, rb, t0, t1, slot in model_balanced_plan(L[members], p.max_seq_len, n, G[n], c):
+            want.append((base[n] + wg, members[bl], rb, t0, t1, slot + 2 * base[n] if slot >= 0 else -1))
+    assert sorted(map(tuple, np.asarray(pieces).tolist())) == sorted(want)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_ragged_class_plan_combine_lookup(seed):
+    """What the combine computes for a split request of a class plan, from
+    its class's groups and the request's offset on the class's line, names
+    exactly the slots its pieces wrote, in order."""
+    p, L, ql, ind, H, q_max = _ragged_case(3 * seed + 1)
+    pieces, grid, used = mla.mla_plan_host_ragged(p, L, ind, int(ind[-1]))
+    if not used:
+        pytest.skip("the uniform plan applies to this batch")
+    nrb = -(-q_max * H // mla.ROWS_PER_BLOCK)
+    NG = grid // nrb
+    nb = np.array([-(-int(q) * H // mla.ROWS_PER_BLOCK) for q in ql])
+    c = mla.PIECE_COST
+    U = np.maximum(1, -(-np.clip(L, 0, p.max_seq_len) // mla.TILE))
+    T = {n: int(sum(c + U[b] for b in range(len(L)) if nb[b] == n)) for n in range(0, 9)}
+    G, base = model_class_plan(T, nrb, min(NG * nrb, p.num_cus), min(-(-NG // 8) * nrb, p.num_cus // 8))
+    by_req = {}
+    for g, b, rb, t0, t1, slot in pieces:
+        by_req.setdefault((b, rb), []).append((t0, slot))
+    for (b, rb), lst in by_req.items():
+        if len(lst) == 1:
+            continue
+        n = nb[b]
+        first = sum(c + U[x] for x in range(b) if nb[x] == n)
+        Tn, Gn = T[n], G[n]
+        start = lambda g: g * Tn // Gn
+        of = lambda v: ((v + 1) * Gn - 1) // Tn
+        g0, g1 = of(first + c), of(first + c + U[b] - 1)
+        got = []
+        for g in range(g0, g1 + 1):
+            if start(g) == start(g + 1):
+                continue
+            second = g == g0 and start(g0) < first
+            got.append(2 * base[n] + 2 * (g * n + rb) + (1 if second else 0))
+        assert got == [s for _, s in sorted(lst)]
