@@ -144,3 +144,36 @@ def test_offsets_beyond_max_q_len_leave_rows_untouched():
     G.compare(o[:4], l[:4], ro[0], rl[0], what="request 0, first four tokens")
     ro1, rl1 = RG.decode(oracle.default(), rg)
     G.compare(o[5:], l[5:], ro1[5:], rl1[5:], what="request 1")
+
+
+# Ragged batches that the row-block class plan takes (balanced mode, at most 8
+# row blocks, requests with fewer than all of them): the plan is confirmed on
+# the host mirror, then the decode is compared with the oracle over the whole
+# output.  (kv, q_max, heads, page, batch, max length, query lengths: None =
+# random in 0..q_max, or one value for every request, seed)
+CLASS_CASES = [
+    ("bf16", 4, 128, 64, 40, 1500, None, 301),
+    ("fp8", 2, 128, 32, 33, 900, None, 302),
+    ("bf16", 4, 128, 64, 24, 2000, 1, 303),      # one class below nrb only
+    ("bf16", 8, 64, 64, 30, 1200, None, 304),     # eight row blocks of 64 heads x 8 tokens
+    ("bf16", 2, 128, 64, 1100, 200, None, 305),   # more requests than the workgroup has threads
+]
+
+
+@pytest.mark.parametrize("case", range(len(CLASS_CASES)))
+def test_class_plan_cases(case):
+    kv, qmax, H, Pg, B, maxlen, ql, seed = CLASS_CASES[case]
+    rng = np.random.default_rng(seed)
+    lens = tuple(int(x) for x in rng.integers(0, maxlen + 1, size=B))
+    inp = P.small(kv=kv, q_len=qmax, heads=H, page_size=Pg, lens=lens, seed=seed,
+                  k_scale=0.5 if kv == "fp8" else None)
+    q_lens = rng.integers(0, qmax + 1, size=B) if ql is None else np.full(B, ql)
+    rg = ragged(inp, q_lens=q_lens)
+    p = mla.make_params(B, qmax, H, Pg, inp.num_pages, inp.block_table.shape[1], inp.max_seq_len,
+                        mla.MLA_KV_FP8_E4M3FN if inp.kv_fp8 else mla.MLA_KV_BF16, inp.softmax_scale,
+                        inp.k_scale, 0, 0, 0)
+    _, _, used = mla.mla_plan_host_ragged(p, inp.seq_lens, rg.qo_indptr, int(rg.qo_indptr[-1]))
+    assert used, "the class plan should apply to this batch"
+    o, l = run_ragged(rg)
+    ro, rl = RG.decode(oracle.default(), rg)
+    G.compare(o, l, ro, rl, fp8=kv == "fp8", what=f"class plan case {case}")
