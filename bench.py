@@ -143,7 +143,7 @@ def kernel_sources_sha256() -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_mla_decode_06_amd", "csrc")
-    for name in ("mla_kernels.hip", "mla_plan.h", "mla_args.h", "mla_rope.h"):
+    for name in ("mla_kernels.hip", "mla_plan.h", "mla_args.h", "mla_rope.h", "mla_fp8.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     with open(os.path.join(ROOT, "paged_mla_decode_06_amd", "build.py"), "rb") as f:
