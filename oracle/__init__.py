@@ -14,6 +14,8 @@ Two independent implementations live here:
 * ``kv_append.py``: the KV-cache append (scatter of new latent rows into the
   pool, with the e4m3fn quantisation of an fp8 pool), pinned by
   ``tests/test_oracle_append.py``.
+* ``query_fp8.py``: the e4m3fn cast of the query in the fp8 decode, pinned by
+  ``tests/test_oracle_query_fp8.py``.
 
 Every function is pinned by the tests in ``tests/test_oracle.py`` (brute
 force, closed forms, invariances, library decoders); no function is left
