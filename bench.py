@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 METRIC = "MLA decode KV-cache GB/s + TFLOPS (% of HBM/MFMA roofline), 128 heads bf16"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8
 
 
 # Timing-only events: no system-scope fence (cache writeback and invalidate)
@@ -200,6 +201,8 @@ def main():
     ap.add_argument("--rotate-gib", type=float, default=1.5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
+    ap.add_argument("--quantize-q-fp8", action="store_true",
+                    help="fp8 pool: cast the query to e4m3fn in the kernel and take fp8 score products")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy kernel of known size (for counter calibration)")
     args = ap.parse_args()
@@ -223,6 +226,11 @@ def main():
     w = WORKLOADS[args.workload]
     inp = generate(w)
     kv_bytes = 1 if inp.kv_fp8 else 2
+    q8 = bool(args.quantize_q_fp8)
+    if q8 and not inp.kv_fp8:
+        print("bench.py: --quantize-q-fp8 needs a workload with an fp8 pool", file=sys.stderr)
+        sys.exit(2)
+    profile_name = w.name + ("_q8" if q8 else "")
     # a ragged batch (per-request query lengths) runs through mla_decode_ragged
     rg = ragged(inp) if w.ragged_q else None
     q_lens = rg.q_lens if rg is not None else np.full(inp.batch, inp.q_len, dtype=np.int32)
@@ -249,7 +257,7 @@ def main():
     lse = torch.empty(out.shape[:-1], dtype=torch.float32, device=dev)
     p = mla.make_params(inp.batch, inp.q_len, inp.heads, inp.page_size, inp.num_pages, inp.block_table.shape[1],
                         inp.max_seq_len, mla.MLA_KV_FP8_E4M3FN if inp.kv_fp8 else mla.MLA_KV_BF16,
-                        inp.softmax_scale, inp.k_scale, min_work_units=w.min_work_units)
+                        inp.softmax_scale, inp.k_scale, min_work_units=w.min_work_units, quantize_q_fp8=int(q8))
     ws = mla.alloc_workspace(p, dev)
     stream = torch.cuda.current_stream()
     ind = torch.from_numpy(rg.qo_indptr).to(dev) if rg is not None else None
@@ -319,14 +327,21 @@ def main():
     # else the dense bf16 MFMA peak; the other fraction is reported beside it.
     split_tflops = flops / (split_ms * 1e-3) / 1e12
     hbm_frac = split_gbs / HBM_PEAK_GBS
-    mfma_frac = split_tflops / MFMA_BF16_PEAK_TFLOPS
-    mfma_bound = flops / split_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    # With the query cast to fp8 the score products (576 of every 1088 flops
+    # per row and token) run at the fp8 peak and the P.V products at the bf16
+    # one: the peak is the flops over the shortest time the two peaks allow.
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS
+    if q8:
+        qk_share = 576.0 / (576.0 + 512.0)
+        mfma_peak = 1.0 / (qk_share / MFMA_FP8_PEAK_TFLOPS + (1.0 - qk_share) / MFMA_BF16_PEAK_TFLOPS)
+    mfma_frac = split_tflops / mfma_peak
+    mfma_bound = flops / split_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     roofline = {"bound": "mfma" if mfma_bound else "hbm",
                 "achieved": round(split_tflops if mfma_bound else split_gbs, 2),
-                "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+                "peak": round(mfma_peak, 1) if mfma_bound else HBM_PEAK_GBS,
                 "unit": "TFLOP/s" if mfma_bound else "GB/s",
                 "frac": round(mfma_frac if mfma_bound else hbm_frac, 4),
-                "traffic": measured_traffic(w.name, whole_call=rg is not None),
+                "traffic": measured_traffic(profile_name, whole_call=rg is not None),
                 "kernel": "mla_split_kernel" if rg is None else "mla_split_kernel + mla_combine_kernel (one call)",
                 "algorithmic_bytes_per_launch": split_bytes, "algorithmic_flops_per_launch": flops,
                 "hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
@@ -349,13 +364,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3fn-kv/bf16" if inp.kv_fp8 else "bf16",
+        "dtype": ("fp8_e4m3fn-kv/fp8-q" if q8 else "fp8_e4m3fn-kv/bf16") if inp.kv_fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": inp.batch,
                    "q_len": f"ragged 1..{inp.q_len}" if rg is not None else inp.q_len, "query_tokens": q_rows,
                    "heads": inp.heads,
                    "page_size": inp.page_size, "kv_dtype": w.kv, "seq_lens": f"{w.lens}", "seed": w.seed,
                    "cached_tokens": int(inp.seq_lens.sum()), "num_pages": inp.num_pages,
+                   "query": "e4m3fn, cast in the kernel" if q8 else "bf16",
                    "rotating_copies": copies},
         "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "kv_gbs": round(kv_only / (ms_step * 1e-3) / 1e9, 2),

@@ -51,7 +51,7 @@ extern "C" {
 
 /* 2: adds mla_decode_qparts(_rope), mla_decode_ragged, mla_check_qo_indptr_host,
  * mla_kv_append(_rope); version 1 entry points and structs are unchanged. */
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 
 typedef enum {
   MLA_OK = 0,
@@ -87,6 +87,17 @@ typedef struct {
                                  split pieces) */
   int32_t num_cus;            /* 0: read the compute-unit count of the current device; n > 0: use n
                                  (lets host-only planning calls run without a device) */
+  int32_t quantize_q_fp8;     /* 0: the query stays bf16 and every score is the exact product of bf16 values
+                                 and dequantised codes (fp32 sums).  1 (an fp8 pool only, else
+                                 MLA_ERR_INVALID_VALUE): the fp8 decode of the pages, which cast the query to
+                                 float8_e4m3fn with q_scale 1 before their fp8 kernel ("tokenspeed
+                                 trtllm_mla.py", TRTLLMMLABackend.forward_decode; "sglang
+                                 trtllm_mla_backend.py", forward_decode and _compute_decode_bmm1_scale): each
+                                 query element, after the rotary embedding when one is applied and rounded to
+                                 bf16, becomes its e4m3fn code (round to nearest even, saturated at +-448,
+                                 NaN stays NaN) and the scores are fp8 x fp8 products summed in fp32.  The
+                                 softmax weights and the output product stay bf16.  A query that already
+                                 holds e4m3fn values (passed as their exact bf16 values) is left unchanged. */
 } mla_decode_params;
 
 /* MLA_ABI_VERSION of the built library. */

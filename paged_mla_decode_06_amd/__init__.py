@@ -46,7 +46,7 @@ class mla_decode_params(ctypes.Structure):
         "batch", "q_len", "num_heads", "kv_lora_rank", "qk_rope_head_dim", "page_size", "num_pages",
         "block_table_stride", "max_seq_len", "kv_dtype")] + [
         ("softmax_scale", ctypes.c_float), ("k_scale", ctypes.c_float)] + [
-        (n, ctypes.c_int32) for n in ("num_splits", "min_work_units", "num_cus")]
+        (n, ctypes.c_int32) for n in ("num_splits", "min_work_units", "num_cus", "quantize_q_fp8")]
 
 
 class mla_query_layout(ctypes.Structure):
@@ -147,15 +147,17 @@ def _check(status: int, what: str) -> None:
 def make_params(batch: int, q_len: int, num_heads: int, page_size: int, num_pages: int, block_table_stride: int,
                 max_seq_len: int, kv_dtype: int = MLA_KV_BF16, softmax_scale: float = 1.0, k_scale: float = 1.0,
                 num_splits: int = 0, min_work_units: int = 0, num_cus: int = 0,
-                kv_lora_rank: int = LATENT_DIM, qk_rope_head_dim: int = ROPE_DIM) -> mla_decode_params:
+                kv_lora_rank: int = LATENT_DIM, qk_rope_head_dim: int = ROPE_DIM,
+                quantize_q_fp8: int = 0) -> mla_decode_params:
     return mla_decode_params(int(batch), int(q_len), int(num_heads), int(kv_lora_rank), int(qk_rope_head_dim),
                              int(page_size), int(num_pages), int(block_table_stride), int(max_seq_len),
                              int(kv_dtype), float(softmax_scale), float(k_scale), int(num_splits),
-                             int(min_work_units), int(num_cus))
+                             int(min_work_units), int(num_cus), int(quantize_q_fp8))
 
 
 def params_for(q, kv_pool, block_table, max_seq_len: int, softmax_scale: float, k_scale: float = 1.0,
-               num_splits: int = 0, min_work_units: int = 0, num_cus: int = 0) -> mla_decode_params:
+               num_splits: int = 0, min_work_units: int = 0, num_cus: int = 0,
+               quantize_q_fp8: bool = False) -> mla_decode_params:
     """Parameters read off the tensor shapes of a decode call."""
     import torch
     B, ql, H, D = q.shape
@@ -165,7 +167,7 @@ def params_for(q, kv_pool, block_table, max_seq_len: int, softmax_scale: float, 
     fp8 = kv_pool.dtype in (torch.float8_e4m3fn, torch.uint8)
     return make_params(B, ql, H, P, N, block_table.stride(0) if block_table.dim() == 2 else 1, max_seq_len,
                        MLA_KV_FP8_E4M3FN if fp8 else MLA_KV_BF16, softmax_scale, k_scale, num_splits,
-                       min_work_units, num_cus)
+                       min_work_units, num_cus, quantize_q_fp8=int(bool(quantize_q_fp8)))
 
 
 def mla_decode_workspace_size(p: mla_decode_params) -> int:
@@ -217,7 +219,7 @@ def _check_decode_shapes(B: int, q_len: int, H: int, kv_pool, block_table, seq_l
 
 def mla_decode(q, kv_pool, block_table, seq_lens, out, lse=None, workspace=None, *, max_seq_len: int,
                softmax_scale: float, k_scale: float = 1.0, num_splits: int = 0, min_work_units: int = 0,
-               stream=None, params: Optional[mla_decode_params] = None):
+               stream=None, params: Optional[mla_decode_params] = None, quantize_q_fp8: bool = False):
     """Enqueue the decode on ``stream`` (default: torch's current stream).
 
     q [B, q_len, H, 576] bf16; kv_pool [N, P, 576] bf16 or float8_e4m3fn;
@@ -245,7 +247,7 @@ def mla_decode(q, kv_pool, block_table, seq_lens, out, lse=None, workspace=None,
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise ValueError("lse must be contiguous float32")
     p = params if params is not None else params_for(q, kv_pool, block_table, max_seq_len, softmax_scale, k_scale,
-                                                     num_splits, min_work_units)
+                                                     num_splits, min_work_units, quantize_q_fp8=quantize_q_fp8)
     if workspace is None:
         workspace = alloc_workspace(p, q.device)
     st = lib().mla_decode(ctypes.byref(p), _ptr(q), _ptr(kv_pool), _ptr(block_table), _ptr(seq_lens), _ptr(out),
@@ -260,7 +262,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # MLA_NOALLOC_SCRATCH_BYTES
 
 def mla_decode_noalloc(q, kv_pool, block_table, seq_lens, out, lse=None, *, max_seq_len: int,
                        softmax_scale: float, k_scale: float = 1.0, num_splits: int = 0, min_work_units: int = 0,
-                       stream=None, params: Optional[mla_decode_params] = None):
+                       stream=None, params: Optional[mla_decode_params] = None, quantize_q_fp8: bool = False):
     """mla_decode with the library's own per-device workspace array: nothing
     is allocated, here or in the library (for graph capture and loops that
     cannot allocate).  Calls that overlap on one device race on that array.
@@ -286,7 +288,7 @@ def mla_decode_noalloc(q, kv_pool, block_table, seq_lens, out, lse=None, *, max_
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise ValueError("lse must be contiguous float32")
     p = params if params is not None else params_for(q, kv_pool, block_table, max_seq_len, softmax_scale, k_scale,
-                                                     num_splits, min_work_units)
+                                                     num_splits, min_work_units, quantize_q_fp8=quantize_q_fp8)
     st = lib().mla_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(kv_pool), _ptr(block_table), _ptr(seq_lens),
                                   _ptr(out), _ptr(lse), _stream_handle(stream))
     _check(st, "mla_decode_noalloc")
@@ -323,7 +325,7 @@ def _rope_struct(positions, cos_sin_cache, is_neox: bool):
 def mla_decode_qparts(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse=None, workspace=None, *,
                       max_seq_len: int, softmax_scale: float, k_scale: float = 1.0, num_splits: int = 0,
                       min_work_units: int = 0, stream=None, positions=None, cos_sin_cache=None,
-                      is_neox: bool = True):
+                      is_neox: bool = True, quantize_q_fp8: bool = False):
     """mla_decode with the query as its latent part q_nope (512 wide) and rope
     part q_rope (64 wide), each [B, q_len, H, w] or [B*q_len, H, w] with any
     token and head strides (multiples of 8 elements): read in place, no
@@ -356,7 +358,8 @@ def mla_decode_qparts(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse=N
     N, P, Dk = kv_pool.shape
     fp8 = kv_pool.dtype in (torch.float8_e4m3fn, torch.uint8)
     p = make_params(B, ql, H, P, N, block_table.stride(0) if block_table.dim() == 2 else 1, max_seq_len,
-                    MLA_KV_FP8_E4M3FN if fp8 else MLA_KV_BF16, softmax_scale, k_scale, num_splits, min_work_units)
+                    MLA_KV_FP8_E4M3FN if fp8 else MLA_KV_BF16, softmax_scale, k_scale, num_splits, min_work_units,
+                    quantize_q_fp8=int(bool(quantize_q_fp8)))
     if workspace is None:
         workspace = alloc_workspace(p, out.device)
     lay = mla_query_layout(int(nt), int(nh), int(rt), int(rh))
@@ -380,7 +383,8 @@ def mla_decode_qparts(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse=N
 def mla_decode_ragged(q, qo_indptr, kv_pool, block_table, seq_lens, out, lse=None, workspace=None, *,
                       max_q_len: int, max_seq_len: int, softmax_scale: float, k_scale: float = 1.0,
                       num_splits: int = 0, min_work_units: int = 0, stream=None,
-                      params: Optional[mla_decode_params] = None, validate: bool = False):
+                      params: Optional[mla_decode_params] = None, validate: bool = False,
+                      quantize_q_fp8: bool = False):
     """Ragged multi-token decode: request b's query tokens are rows
     qo_indptr[b] .. qo_indptr[b+1]-1 of the packed q [T, H, 576] bf16
     (qo_indptr int32 [B+1] on the GPU, at most max_q_len per request); out
@@ -425,7 +429,8 @@ def mla_decode_ragged(q, qo_indptr, kv_pool, block_table, seq_lens, out, lse=Non
     fp8 = kv_pool.dtype in (torch.float8_e4m3fn, torch.uint8)
     p = params if params is not None else make_params(
         B, max_q_len, H, P, N, block_table.stride(0) if block_table.dim() == 2 else 1, max_seq_len,
-        MLA_KV_FP8_E4M3FN if fp8 else MLA_KV_BF16, softmax_scale, k_scale, num_splits, min_work_units)
+        MLA_KV_FP8_E4M3FN if fp8 else MLA_KV_BF16, softmax_scale, k_scale, num_splits, min_work_units,
+        quantize_q_fp8=int(bool(quantize_q_fp8)))
     if validate:
         ind_host = qo_indptr.cpu().numpy()
         _check(mla_check_qo_indptr_host(p, ind_host, T), "mla_decode_ragged: qo_indptr")

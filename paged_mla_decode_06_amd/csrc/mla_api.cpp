@@ -57,6 +57,15 @@ mla_status device_info(DeviceInfo* out) {
 
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.f; }
 
+// How the split kernel takes the pool's elements (the kKv* modes of the kernels).
+#ifndef MLA_F8_EXACT_MODE
+#define MLA_F8_EXACT_MODE 1
+#endif
+int kv_mode(const mla_decode_params* p) {
+  if (p->kv_dtype != MLA_KV_FP8_E4M3FN) return 0;
+  return p->quantize_q_fp8 ? 2 : MLA_F8_EXACT_MODE;
+}
+
 // Checks that need no device.  Returns MLA_OK or the error.
 mla_status check_params(const mla_decode_params* p) {
   if (p == nullptr) return MLA_ERR_INVALID_VALUE;
@@ -74,6 +83,8 @@ mla_status check_params(const mla_decode_params* p) {
   if (p->kv_dtype == MLA_KV_FP8_E4M3FN && !finite_pos(p->k_scale)) return MLA_ERR_INVALID_VALUE;
   if (p->num_splits < 0 || p->num_splits > kMaxSplits) return MLA_ERR_INVALID_VALUE;
   if (p->min_work_units < 0 || p->num_cus < 0) return MLA_ERR_INVALID_VALUE;
+  if (p->quantize_q_fp8 != 0 && (p->quantize_q_fp8 != 1 || p->kv_dtype != MLA_KV_FP8_E4M3FN))
+    return MLA_ERR_INVALID_VALUE;
   // Work units and the balanced plan's cost positions are counted in int32 on the device.
   const int64_t nrb = mla::row_blocks(p->q_len, p->num_heads);
   if ((int64_t)p->batch * nrb * mla::positions_of(p->max_seq_len) >= ((int64_t)1 << 31)) return MLA_ERR_NOT_SUPPORTED;
@@ -257,7 +268,7 @@ static mla_status decode_impl(const mla_decode_params* p, const QueryParts& qp, 
   a.out_scale = kscale;
   hipStream_t st = (hipStream_t)stream;
   if (ev_start != nullptr && hipEventRecord((hipEvent_t)ev_start, st) != hipSuccess) return MLA_ERR_HIP;
-  if (mla_launch_split(&a, fp8 ? 1 : 0, st) != hipSuccess) return MLA_ERR_HIP;
+  if (mla_launch_split(&a, kv_mode(p), st) != hipSuccess) return MLA_ERR_HIP;
   if (ev_mid != nullptr && hipEventRecord((hipEvent_t)ev_mid, st) != hipSuccess) return MLA_ERR_HIP;
   if (p->num_splits != 1) {
     mla::CombineArgs c;

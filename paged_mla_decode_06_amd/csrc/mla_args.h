@@ -74,7 +74,10 @@ struct AppendArgs {
 }  // namespace mla
 
 extern "C" {
-hipError_t mla_launch_split(const mla::SplitArgs* a, int fp8, hipStream_t stream);
+// kv_mode: 0 bf16 pool; 1 fp8 pool converted by the loaders; 2 fp8 pool with
+// the query quantised and fp8 products; 3 fp8 pool converted at the fragment
+// reads.
+hipError_t mla_launch_split(const mla::SplitArgs* a, int kv_mode, hipStream_t stream);
 hipError_t mla_launch_combine(const mla::CombineArgs* a, hipStream_t stream);
 hipError_t mla_launch_gather(const void* pool, const int32_t* bt, const int32_t* seq_lens, int32_t W, int32_t P,
                              int32_t N, int32_t max_seq_len, int32_t b, int32_t elem_bytes, void* dst,

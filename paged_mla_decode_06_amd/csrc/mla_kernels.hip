@@ -24,6 +24,7 @@
 #include <stdint.h>
 
 #include "mla_args.h"
+#include "mla_fp8.h"
 #include "mla_plan.h"
 #include "mla_rope.h"
 
@@ -106,6 +107,19 @@ constexpr float kLn2 = 0.6931471805599453f;
 // A row's running maximum is raised only when a tile's maximum exceeds it by
 // more than this (log2 units); exponentials stay <= 2^8, exact math unchanged.
 constexpr float kRescaleSlack = 8.0f;
+// How the pool's elements reach the matrix unit (the KV template parameter
+// of the split kernel):
+//   kKvBf16     bf16 pool: bf16 tiles in LDS, bf16 products.
+//   kKvFp8Cvt   e4m3fn pool: the loader waves convert the codes to bf16 on
+//               their way into LDS (exactly), bf16 products.
+//   kKvFp8Tile  e4m3fn pool: the codes are staged in LDS as they are, and K
+//               and V^T are converted to bf16 (exactly) as their MFMA
+//               fragments are read; bf16 products.
+//   kKvFp8Q     e4m3fn pool, codes staged as they are; the query rows are
+//               quantised to e4m3fn and the scores are fp8 products; V^T is
+//               converted to bf16 at its fragment read.
+constexpr int kKvBf16 = 0, kKvFp8Cvt = 1, kKvFp8Q = 2, kKvFp8Tile = 3;
+constexpr bool fp8_tile(int kv) { return kv == kKvFp8Q || kv == kKvFp8Tile; }
 
 static_assert(kChunks % 64 == 0, "tile must be a whole number of wave-wide loads");
 static_assert(kTileLoads % kLoaderWaves == 0, "every loader wave issues the same number of tile loads");
@@ -283,11 +297,11 @@ struct PageWindow {
 // lane picks the global chunk whose swizzled LDS position is its own.  Lanes
 // of rows past the piece's last token issue no load: those LDS rows keep
 // zeros or an earlier tile's (finite) rows, and their scores are masked.
-template <bool FP8>
+template <int KV>
 struct Stage;
 
 template <>
-struct Stage<false> {
+struct Stage<0> {
   // Load i of loader wave w fills the 64 physical LDS chunks starting at
   // P = 64*(w + kLoaderWaves*i).  The chunk p = P + l of lane l holds logical
   // chunk (p mod 72) ^ z(r) of row r = p / 72, z(r) = swz(r), so its
@@ -341,7 +355,7 @@ struct Stage<false> {
     const uint32_t dst = (uint32_t)(uintptr_t)(buf + wave * 1024);
     // Opaque copies: the offsets are unpacked here, once per tile, instead of
     // being hoisted out of the tile loop as nine live registers.
-    Stage<false> o = *this;
+    Stage<0> o = *this;
 #pragma unroll
     for (int j = 0; j < kPacked; j++) asm("" : "+v"(o.xoff[j]));
     if (ts + kTile <= tok_end) {
@@ -400,7 +414,7 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
 // rows of a tile are consecutive slots of one page, so chunk m of row r is
 // at byte 576*r + 16*m of the tile's first row.
 template <>
-struct Stage<true> {
+struct Stage<1> {
   static constexpr int kChunks = kTile * kRowDim / 16;   // 1152
   static constexpr int kRowChunks = kRowDim / 16;        // 36
   static constexpr int kPer = (kChunks + kLoaderThreads - 1) / kLoaderThreads;   // 5
@@ -468,6 +482,97 @@ struct Stage<true> {
     }
   }
 };
+
+// fp8 pool, codes staged as they are (kKvFp8Tile, kKvFp8Q): a tile is 32
+// rows of 576 bytes (36 16-byte chunks) in the first half of its ring buffer.
+// Logical chunk c of row r sits at physical chunk c ^ swz8(r): only the low
+// two bits change, so a chunk stays inside its aligned group of four (36 is
+// a multiple of four).  The compute waves read the tile in 8-byte pieces: the
+// K fragments (8 bytes of 16 consecutive rows per 16 lanes) and the 8-bit
+// transposing V reads (8 bytes of 8 rows per 16 lanes, two lanes to a row).
+// With the 576-byte pitch and swz8(r) = (r/4) mod 4, and the second 16-token
+// block of K taken in the row order 16 + (i ^ 8), both read at the rate of
+// conflict-free linear 8-byte reads (measured on gfx950 against other
+// swizzles and row orders, which ran 20-130 % slower).
+__device__ __forceinline__ int swz8(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int lds_off8(int r, int c) { return r * kRowDim + ((c ^ swz8(r)) << 4); }
+constexpr int kTile8Bytes = kTile * kRowDim;                    // 18432
+constexpr int kLoaders8 = 2;                                    // loader waves issuing fp8 tile loads
+constexpr int kLoads8 = kTile8Bytes / 1024 / kLoaders8;         // 9 wave-wide 1 KB loads each
+static_assert(kLoads8 == kLoadsPerWave, "the fp8 tile loads share the bf16 tile's wait counts");
+static_assert(kTile8Bytes % (1024 * kLoaders8) == 0 && (kRowDim / 16) % 4 == 0, "fp8 tile staging");
+
+// Loader wave lw < kLoaders8, load i fills the 64 physical chunks starting at
+// 64*(lw + kLoaders8*i): lane l's chunk p holds logical chunk
+// (p mod 36) ^ swz8(r) of row r = p / 36, at byte 576r + 16c of the tile's
+// contiguous run in the pool (< 2^16: two offsets to a register).  The other
+// loader waves issue nothing for an fp8 tile.
+struct Stage8 {
+  static constexpr int kPacked = (kLoads8 + 1) / 2;
+  uint32_t xoff[kPacked];
+  __device__ __forceinline__ static int first_chunk(int lw, int i) { return 64 * (lw + kLoaders8 * i); }
+  __device__ __forceinline__ void init(int lw) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < kPacked; j++) xoff[j] = 0;
+    if (lw >= kLoaders8) return;
+#pragma unroll
+    for (int i = 0; i < kLoads8; i++) {
+      const int p = first_chunk(lw, i) + lane;
+      const int r = p / 36;
+      const int c = (p - 36 * r) ^ swz8(r);
+      xoff[i / 2] |= (uint32_t)(r * kRowDim + 16 * c) << (16 * (i % 2));
+    }
+  }
+  __device__ __forceinline__ uint32_t lane_off(int i) const { return (xoff[i / 2] >> (16 * (i % 2))) & 0xFFFFu; }
+  // As Stage<0>::issue: kLoads8 loads per issuing wave for a tile with a
+  // valid token (rows past the last one re-read the same chunk of row 0; a
+  // block-table entry outside [0, N) reads page 0), zeros for a tile
+  // without one.
+  __device__ __forceinline__ int issue(const SplitArgs& a, lds_char* buf, PageWindow& pw, int b, int ts, int tok_end,
+                                       int lw) const {
+    if (lw >= kLoaders8) return 0;
+    b = __builtin_amdgcn_readfirstlane(b);
+    ts = __builtin_amdgcn_readfirstlane(ts);
+    tok_end = __builtin_amdgcn_readfirstlane(tok_end);
+    const int lane = threadIdx.x & 63;
+    if (ts >= tok_end) {
+#pragma unroll
+      for (int i = 0; i < kLoads8; i++)
+        *(__attribute__((address_space(3))) u32x4_t*)(buf + 1024 * (lw + kLoaders8 * i) + 16 * lane) =
+            u32x4_t{0u, 0u, 0u, 0u};
+      return 0;
+    }
+    const int32_t page = pw.page(a, b, ts >> a.p_shift);
+    const int32_t pg = (uint32_t)page < (uint32_t)a.N ? page : 0;
+    const char* base = (const char*)a.pool + (((int64_t)pg << a.p_shift) + (ts & (a.P - 1))) * (int64_t)kRowDim;
+    const uint32_t dst = (uint32_t)(uintptr_t)(buf + 1024 * lw);
+    Stage8 o = *this;
+#pragma unroll
+    for (int j = 0; j < kPacked; j++) asm("" : "+v"(o.xoff[j]));
+    if (ts + kTile <= tok_end) {
+#pragma unroll
+      for (int i = 0; i < kLoads8; i++) dma16(base, o.lane_off(i), dst + 1024 * kLoaders8 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLoads8; i++) {
+        const int r = (first_chunk(lw, i) + lane) / 36;
+        const uint32_t off = o.lane_off(i) - (ts + r < tok_end ? 0u : (uint32_t)(r * kRowDim));
+        dma16(base, off, dst + 1024 * kLoaders8 * i);
+      }
+    }
+    return kLoads8;
+  }
+  __device__ __forceinline__ void wait(int later) const {
+    if (later >= 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+};
+template <>
+struct Stage<kKvFp8Tile> : Stage8 {};
+template <>
+struct Stage<kKvFp8Q> : Stage8 {};
 
 #ifndef MLA_PERMLANE
 #define MLA_PERMLANE 1
@@ -571,6 +676,55 @@ struct LaneOffsets {
   }
 };
 
+// The same for a tile of fp8 codes (lds_off8).
+//  K fragment of step k (dims 32k + 8g .. +8 of the lane's token, 8 codes):
+//    token i16 of the first 16-token block and 16 + (i16 ^ 8) of the second
+//    (tb), at kbase[tb][k&1] + 64*(k>>1).
+//  V^T block mb (one 8-bit transposing read): lane 16G + 2m + h reads 8
+//    codes of token tok(G, m), dims 16mb + 8h .. +8, where tok(G, m) is
+//    4G + m for m < 4 and 16 + ((4G + m - 4) ^ 8) otherwise: the order of
+//    the lane's eight scores.  The hardware hands lane j of the group dim
+//    16mb + j of the group's 8 tokens.  At vbase[mb&3] + 64*(mb>>2).
+struct LaneOffsets8 {
+  int kbase[2][2];
+  int vbase[4];
+  __device__ __forceinline__ void init() {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int tb = 0; tb < 2; tb++) {
+      const int r = tb ? 16 + (i16 ^ 8) : i16;
+#pragma unroll
+      for (int e = 0; e < 2; e++) kbase[tb][e] = r * kRowDim + 16 * ((2 * e + (g >> 1)) ^ swz8(r)) + 8 * (g & 1);
+    }
+    const int h = i16 & 1, m = i16 >> 1;
+    const int r = m < 4 ? 4 * g + m : 16 + ((4 * g + m - 4) ^ 8);
+#pragma unroll
+    for (int m4 = 0; m4 < 4; m4++) vbase[m4] = r * kRowDim + 16 * (m4 ^ swz8(r)) + 8 * h;
+  }
+};
+template <int KV>
+struct LaneOffsetsSel {
+  typedef LaneOffsets type;
+};
+template <>
+struct LaneOffsetsSel<kKvFp8Tile> {
+  typedef LaneOffsets8 type;
+};
+template <>
+struct LaneOffsetsSel<kKvFp8Q> {
+  typedef LaneOffsets8 type;
+};
+template <int KV>
+using LaneOffsetsOf = typename LaneOffsetsSel<KV>::type;
+
+// Eight e4m3fn codes (two words, code e in byte e%4 of word e/4) to the
+// bf16x8 fragment of their values.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(u32x2_t w) {
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
+                                              fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1])});
+}
+
 // QK wave, one tile: S^T[32 tokens x 16 rows] = K_tile . Q^T (36 MFMA), the
 // K reads kKAhead steps ahead of their MFMA.  Lane l ends with the scores of
 // row l%16 for tokens 4g + r (s0[r]) and 16 + 4g + r (s1[r]), g = l/16.
@@ -610,10 +764,121 @@ __device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[kQSteps], lds_cchar
   }
 }
 
+// QK wave, one tile of fp8 codes, bf16 products: as qk_tile, each K
+// fragment read as 8 codes and converted to bf16 (exactly) before its MFMA.
+// s1[r] is the score of token 16 + ((4g + r) ^ 8).
+template <int kKAhead, int kSChains>
+__device__ __forceinline__ void qk_tile_cvt(const bf16x8_t (&qf)[kQSteps], lds_cchar* cur, const LaneOffsets8& lo_,
+                                            f32x4v_t& s0, f32x4v_t& s1) {
+  static_assert(kSChains == 2 || kSChains == 4, "one or two accumulation chains per token block");
+  constexpr int kCh = kSChains / 2;
+  lds_cchar* kp[2][2] = {{opaque_lds(cur + lo_.kbase[0][0]), opaque_lds(cur + lo_.kbase[0][1])},
+                         {opaque_lds(cur + lo_.kbase[1][0]), opaque_lds(cur + lo_.kbase[1][1])}};
+  auto kread = [&](int s) -> u32x2_t {
+    const int k = s >> 1, tb = s & 1;
+    return *(__attribute__((address_space(3))) const u32x2_t*)(kp[tb][k & 1] + 64 * (k >> 1));
+  };
+  u32x2_t kb[kKAhead];
+#pragma unroll
+  for (int s = 0; s < kKAhead; s++) kb[s] = kread(s);
+  f32x4v_t sp[2][kCh];
+#pragma unroll
+  for (int tb = 0; tb < 2; tb++)
+#pragma unroll
+    for (int c = 0; c < kCh; c++) sp[tb][c] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kQKSteps; s++) {
+    const bf16x8_t kf = fp8x8_to_bf16x8(kb[s % kKAhead]);
+    if (s + kKAhead < kQKSteps) kb[s % kKAhead] = kread(s + kKAhead);
+    const int k = s >> 1, tb = s & 1;
+    sp[tb][k % kCh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[k], sp[tb][k % kCh], 0, 0, 0);
+    if (MLA_PIN_ORDER) __builtin_amdgcn_sched_barrier(0);
+  }
+  s0 = sp[0][0];
+  s1 = sp[1][0];
+  if constexpr (kCh == 2) {
+    s0 += sp[0][1];
+    s1 += sp[1][1];
+  }
+}
+
+// The query rows of a QK wave as e4m3fn codes, in the k order of the fp8
+// MFMAs: main[kb] is the B operand of 16x16x128 step kb (dims 128kb ..
+// +128): lane l (row l%16, g = l/16) holds in bytes 8j .. 8j+7 dims
+// 32(4kb + j) + 8g .. +8, the dims its K fragment of step 4kb + j holds, so
+// the k order inside the MFMA is the same for both operands.  rope[s] is the
+// B operand of 16x16x32 step s over the rope dims 512 + 32s .. +32 (lane
+// bytes = dims 512 + 32s + 8g .. +8).
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+struct QCodes {
+  i32x8_t main[4];
+  u32x2_t rope[2];
+};
+
+// Eight bf16 query values to their e4m3fn codes (two words).
+__device__ __forceinline__ u32x2_t bf16x8_to_e4m3(u32x4_t v) {
+  auto lo = [](uint32_t w) { return __builtin_bit_cast(float, w << 16); };
+  auto hi = [](uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); };
+  return u32x2_t{e4m3fn_x4(lo(v[0]), hi(v[0]), lo(v[1]), hi(v[1])), e4m3fn_x4(lo(v[2]), hi(v[2]), lo(v[3]), hi(v[3]))};
+}
+
+// QK wave, one tile of fp8 codes, fp8 products: per 16-token block four
+// 16x16x128 MFMAs over the 512 latent dims (each fed by four 8-byte K
+// fragment reads) and two 16x16x32 ones over the 64 rope dims, the two
+// blocks' accumulations alternating, operands read two MFMAs ahead.
+// s1[r] is the score of token 16 + ((4g + r) ^ 8).
+__device__ __forceinline__ void qk_tile_q8(const QCodes& q8, lds_cchar* cur, const LaneOffsets8& lo_, f32x4v_t& s0,
+                                           f32x4v_t& s1) {
+  typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
+  lds_cchar* kp[2][2] = {{opaque_lds(cur + lo_.kbase[0][0]), opaque_lds(cur + lo_.kbase[0][1])},
+                         {opaque_lds(cur + lo_.kbase[1][0]), opaque_lds(cur + lo_.kbase[1][1])}};
+  auto kread = [&](int tb, int k) -> u32x2_t {
+    return *(__attribute__((address_space(3))) const u32x2_t*)(kp[tb][k & 1] + 64 * (k >> 1));
+  };
+  // MFMAs i = 0..7: 16x16x128 step kb = i/2 of block tb = i%2; i = 8..11:
+  // 16x16x32 rope step s = (i-8)/2 of block tb = i%2
+  constexpr int kOps = 12, kAhead = 2;
+  i32x8_t A[kAhead + 1];
+  u32x2_t R[2][2];
+  auto fetch = [&](int i) {
+    const int tb = i & 1;
+    if (i < 8) {
+      const int kb = i >> 1;
+      const u32x2_t r0 = kread(tb, 4 * kb), r1 = kread(tb, 4 * kb + 1), r2 = kread(tb, 4 * kb + 2),
+                    r3 = kread(tb, 4 * kb + 3);
+      A[i % (kAhead + 1)] = __builtin_bit_cast(i32x8_t, u32x8_t{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]});
+    } else {
+      R[tb][(i - 8) >> 1] = kread(tb, 16 + ((i - 8) >> 1));
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kAhead; i++) fetch(i);
+  f32x4v_t sp[2] = {f32x4v_t{0.f, 0.f, 0.f, 0.f}, f32x4v_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int i = 0; i < kOps; i++) {
+    if (i + kAhead < kOps) fetch(i + kAhead);
+    const int tb = i & 1;
+    if (i < 8) {
+      // e4m3 operands (format 0 for both), unit scales (E8M0 127)
+      sp[tb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[i % (kAhead + 1)], q8.main[i >> 1], sp[tb], 0, 0,
+                                                                 0, 127, 0, 127);
+    } else {
+      const int st = (i - 8) >> 1;
+      sp[tb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, R[tb][st]),
+                                                          __builtin_bit_cast(long, q8.rope[st]), sp[tb], 0, 0, 0);
+    }
+    if (MLA_PIN_ORDER) __builtin_amdgcn_sched_barrier(0);
+  }
+  s0 = sp[0];
+  s1 = sp[1];
+}
+
 // QK wave, one tile: the online softmax of the lane's 8 scores of its row.
 // The bf16 weights go to LDS as the lane's 16-byte B operand of the PV MFMA
 // (tokens in the order of the scores: the V^T reads follow the same order),
 // and the factor by which the row's running output is to be rescaled.
+// kTb1Perm: s1[r] holds token 16 + ((4g + r) ^ 8) (fp8 tiles), else 16 + 4g + r.
+template <bool kTb1Perm>
 __device__ __forceinline__ void softmax_tile(f32x4v_t s0, f32x4v_t s1, float& m_run, float& l_run, int ts, int limit,
                                              int lim_min, float scale_log2, lds_char* pout, lds_char* aout) {
   const int lane = threadIdx.x & 63;
@@ -626,7 +891,7 @@ __device__ __forceinline__ void softmax_tile(f32x4v_t s0, f32x4v_t s1, float& m_
   if (ts + kTile > lim_min) {
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-      const int t = ts + 16 * (e >> 2) + 4 * g + (e & 3);
+      const int t = e < 4 ? ts + 4 * g + e : ts + 16 + (kTb1Perm ? ((4 * g + (e & 3)) ^ 8) : 4 * g + (e & 3));
       sv[e] = t < limit ? sv[e] : kNegInf;
     }
   }
@@ -714,6 +979,50 @@ __device__ __forceinline__ void pv_tile(f32x4v_t (&acc)[kPVRowGroups][kPVBlocks]
   }
 }
 
+// PV wave, one tile of fp8 codes: as pv_tile, each V^T block one 8-bit
+// transposing read of 8 codes per lane, converted to bf16 (exactly) before
+// its MFMAs.
+template <int kVAhead>
+__device__ __forceinline__ void pv_tile8(f32x4v_t (&acc)[kPVRowGroups][kPVBlocks], lds_cchar* vcur,
+                                         const LaneOffsets8& lo_, lds_cchar* pin, lds_cchar* ain) {
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  const int lane = threadIdx.x & 63;
+  lds_cchar* vp[4] = {opaque_lds(vcur + lo_.vbase[0]), opaque_lds(vcur + lo_.vbase[1]),
+                      opaque_lds(vcur + lo_.vbase[2]), opaque_lds(vcur + lo_.vbase[3])};
+  auto vread = [&](int mb) -> u32x2_t {
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                           (__attribute__((address_space(3))) i32x2_t*)(vp[mb & 3] + 64 * (mb >> 2))));
+  };
+  u32x2_t vb[kVAhead];
+#pragma unroll
+  for (int m = 0; m < kVAhead; m++) vb[m] = vread(m);
+  bf16x8_t pf[kPVRowGroups];
+#pragma unroll
+  for (int r = 0; r < kPVRowGroups; r++)
+    pf[r] = *(__attribute__((address_space(3))) const bf16x8_t*)(pin + 1024 * r + 16 * lane);
+  float alpha[kPVRowGroups];
+#pragma unroll
+  for (int r = 0; r < kPVRowGroups; r++) alpha[r] = ((__attribute__((address_space(3))) const float*)ain)[r];
+  bool any = false;
+#pragma unroll
+  for (int r = 0; r < kPVRowGroups; r++) any |= alpha[r] != 1.f;
+  if (__any(any)) {
+#pragma unroll
+    for (int r = 0; r < kPVRowGroups; r++)
+#pragma unroll
+      for (int mb = 0; mb < kPVBlocks; mb++) acc[r][mb] *= alpha[r];
+  }
+#pragma unroll
+  for (int mb = 0; mb < kPVBlocks; mb++) {
+    const bf16x8_t vf = fp8x8_to_bf16x8(vb[mb % kVAhead]);
+    if (mb + kVAhead < kPVBlocks) vb[mb % kVAhead] = vread(mb + kVAhead);
+#pragma unroll
+    for (int r = 0; r < kPVRowGroups; r++)
+      acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[r], acc[r][mb], 0, 0, 0);
+    if (MLA_PIN_ORDER) __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // The pipeline of one piece runs in intervals j = -1 .. nt-1, each opened by
 // a workgroup barrier; in interval j the QK waves take tile j+1, the PV waves
 // tile j, and the loaders issue tile j+3 into the buffer of tile j-1 (free:
@@ -725,15 +1034,15 @@ __device__ __forceinline__ void pv_tile(f32x4v_t (&acc)[kPVRowGroups][kPVBlocks]
 __device__ __forceinline__ int tile_buf(int t) { return t & (kTileBufs - 1); }
 static_assert((kTileBufs & (kTileBufs - 1)) == 0, "tile_buf masks the tile index");
 
-template <bool FP8>
-__device__ void load_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, const Piece& pc, int lw) {
+template <int KV>
+__device__ void load_piece(const SplitArgs& a, lds_char* lds, Stage<KV>& stg, const Piece& pc, int lw) {
   const int b = pc.b;
   const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
   const int tok_end = min(pc.tile1 * kTile, L);
   const int nt = pc.tile1 - pc.tile0;
   PageWindow pw;
   pw.init(a, b, (pc.tile0 * kTile) >> a.p_shift, (tok_end + a.P - 1) >> a.p_shift);
-  if constexpr (FP8) {
+  if constexpr (KV == kKvFp8Cvt) {
 #if MLA_F8_DEFER
     // fp8 codes go through registers: tile t's codes are loaded in interval
     // t-3 and converted into LDS in interval t-2 (its buffer is free from
@@ -782,8 +1091,8 @@ __device__ void load_piece(const SplitArgs& a, lds_char* lds, Stage<FP8>& stg, c
 
 // The QK waves' side of one piece: the scores and the online softmax of the
 // wave's 16 rows.
-template <bool FP8, bool RAGGED>
-__device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& lo_, const Piece& pc, int w) {
+template <int KV, bool RAGGED>
+__device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsetsOf<KV>& lo_, const Piece& pc, int w) {
   const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
   const int b = pc.b;
   const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
@@ -825,17 +1134,38 @@ __device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
 #pragma unroll
     for (int k = 0; k < kQSteps; k++) qf[k] = __builtin_bit_cast(bf16x8_t, row_ok ? qv[k] : u32x4_t{0u, 0u, 0u, 0u});
   }
+  // fp8 products: the rows (rotated, when a rotary embedding applies) as
+  // e4m3fn codes of their bf16 values, scale 1
+  QCodes q8;
+  if constexpr (KV == kKvFp8Q) {
+    typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
+    u32x2_t c[kQSteps];
+#pragma unroll
+    for (int k = 0; k < kQSteps; k++) c[k] = bf16x8_to_e4m3(__builtin_bit_cast(u32x4_t, qf[k]));
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+      q8.main[kb] = __builtin_bit_cast(i32x8_t, u32x8_t{c[4 * kb][0], c[4 * kb][1], c[4 * kb + 1][0], c[4 * kb + 1][1],
+                                                        c[4 * kb + 2][0], c[4 * kb + 2][1], c[4 * kb + 3][0],
+                                                        c[4 * kb + 3][1]});
+    q8.rope[0] = c[16];
+    q8.rope[1] = c[17];
+  }
   float m_run = kNegInf, l_run = 0.f;
   for (int j = -1; j < nt; j++) {
     lds_barrier();
     const int t = j + 1;
     if (t < nt) {
       f32x4v_t s0, s1;
-      if constexpr (FP8)
-        qk_tile<MLA_F8_KA, MLA_F8_SC>(qf, lds + tile_buf(t) * kTileBytes, lo_, s0, s1);
+      lds_cchar* cur = lds + tile_buf(t) * kTileBytes;
+      if constexpr (KV == kKvFp8Q)
+        qk_tile_q8(q8, cur, lo_, s0, s1);
+      else if constexpr (KV == kKvFp8Tile)
+        qk_tile_cvt<MLA_F8_KA, MLA_F8_SC>(qf, cur, lo_, s0, s1);
+      else if constexpr (KV == kKvFp8Cvt)
+        qk_tile<MLA_F8_KA, MLA_F8_SC>(qf, cur, lo_, s0, s1);
       else
-        qk_tile<MLA_KA, MLA_SC>(qf, lds + tile_buf(t) * kTileBytes, lo_, s0, s1);
-      softmax_tile(s0, s1, m_run, l_run, (pc.tile0 + t) * kTile, limit, lim_min, a.scale_log2,
+        qk_tile<MLA_KA, MLA_SC>(qf, cur, lo_, s0, s1);
+      softmax_tile<fp8_tile(KV)>(s0, s1, m_run, l_run, (pc.tile0 + t) * kTile, limit, lim_min, a.scale_log2,
                    lds + kPBufOff + ((t & 1) * kRowGroups + w) * 1024,
                    lds + kABufOff + (t & 1) * (kRowsPerBlock * 4) + 16 * i16 + 4 * w);
     }
@@ -853,8 +1183,8 @@ __device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
 
 // The PV waves' side of one piece: the output rows, written with the LSE (or
 // as a partial result).
-template <bool FP8, bool RAGGED>
-__device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& lo_, const Piece& pc, int v) {
+template <int KV, bool RAGGED>
+__device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsetsOf<KV>& lo_, const Piece& pc, int v) {
   const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
   const int b = pc.b;
   const int nt = pc.tile1 - pc.tile0;
@@ -868,10 +1198,12 @@ __device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsets& l
   for (int j = -1; j < nt; j++) {
     lds_barrier();
     if (j >= 0) {
-      lds_cchar* vcur = lds + tile_buf(j) * kTileBytes + 32 * mb0;
+      lds_cchar* vcur = lds + tile_buf(j) * kTileBytes + (fp8_tile(KV) ? 16 : 32) * mb0;
       lds_cchar* pin = lds + kPBufOff + ((j & 1) * kRowGroups + rg0) * 1024;
       lds_cchar* ain = lds + kABufOff + (j & 1) * (kRowsPerBlock * 4) + 16 * i16 + 4 * rg0;
-      if constexpr (FP8)
+      if constexpr (fp8_tile(KV))
+        pv_tile8<MLA_F8_VA>(acc, vcur, lo_, pin, ain);
+      else if constexpr (KV == kKvFp8Cvt)
         pv_tile<MLA_F8_VA>(acc, vcur, lo_, pin, ain);
       else
         pv_tile<MLA_VA>(acc, vcur, lo_, pin, ain);
@@ -1148,7 +1480,7 @@ __device__ __forceinline__ bool class_start(const SplitArgs& a, char* smem, Walk
 // Every wave of a workgroup walks the same pieces: the loader waves fill the
 // tile ring, the compute waves consume it; their barriers pair up one to one.
 // ws.grp: the first plan group of the launched group (forced mode: its only one).
-template <bool FP8, bool RAGGED, class PieceFn>
+template <bool RAGGED, class PieceFn>
 __device__ __forceinline__ void for_each_piece(const SplitArgs& a, const WalkStart& ws, PieceFn&& fn_all) {
   // A ragged batch's request with fewer query rows than this row block's
   // first has nothing here: every wave of the workgroup skips the piece.
@@ -1182,7 +1514,7 @@ __device__ __forceinline__ void for_each_piece(const SplitArgs& a, const WalkSta
 
 // RAGGED: per-request query lengths from a.qo_indptr (a separate
 // instantiation, so the uniform batch's code is what it was without them).
-template <bool FP8, bool RAGGED>
+template <int KV, bool RAGGED>
 __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   lds_char* tiles = (lds_char*)smem;
@@ -1233,21 +1565,18 @@ __global__ __launch_bounds__(kSplitThreads, 1) void mla_split_kernel(SplitArgs a
   if (wave >= kLoaderWave0) {
     if (MLA_PRIO_LD) __builtin_amdgcn_s_setprio(MLA_PRIO_LD);
     const int lw = wave - kLoaderWave0;
-    Stage<FP8> stg;
+    Stage<KV> stg;
     stg.init(lw);
-    for_each_piece<FP8, RAGGED>(a, ws,
-                                [&](const Piece& pc) { load_piece<FP8>(a, tiles, stg, pc, lw); });
+    for_each_piece<RAGGED>(a, ws, [&](const Piece& pc) { load_piece<KV>(a, tiles, stg, pc, lw); });
   } else if (wave >= kPVWave0) {
-    LaneOffsets lo_;
+    LaneOffsetsOf<KV> lo_;
     lo_.init();
-    for_each_piece<FP8, RAGGED>(a, ws,
-                                [&](const Piece& pc) { pv_piece<FP8, RAGGED>(a, tiles, lo_, pc, wave - kPVWave0); });
+    for_each_piece<RAGGED>(a, ws, [&](const Piece& pc) { pv_piece<KV, RAGGED>(a, tiles, lo_, pc, wave - kPVWave0); });
   } else {
     if (MLA_PRIO_QK) __builtin_amdgcn_s_setprio(MLA_PRIO_QK);
-    LaneOffsets lo_;
+    LaneOffsetsOf<KV> lo_;
     lo_.init();
-    for_each_piece<FP8, RAGGED>(a, ws,
-                                [&](const Piece& pc) { qk_piece<FP8, RAGGED>(a, tiles, lo_, pc, wave - kQKWave0); });
+    for_each_piece<RAGGED>(a, ws, [&](const Piece& pc) { qk_piece<KV, RAGGED>(a, tiles, lo_, pc, wave - kQKWave0); });
   }
 }
 
@@ -1537,13 +1866,16 @@ size_t mla_split_lds_bytes(int32_t B, int32_t num_splits) {
   return (size_t)mla::kSplitLdsBytes;
 }
 
-hipError_t mla_launch_split(const mla::SplitArgs* a, int fp8, hipStream_t stream) {
+hipError_t mla_launch_split(const mla::SplitArgs* a, int kv_mode, hipStream_t stream) {
+  if (kv_mode < 0 || kv_mode > 3) return hipErrorInvalidValue;
   const size_t lds = mla_split_lds_bytes(a->B, a->num_splits);
   const bool ragged = a->qo_indptr != nullptr;
-  const int v = (fp8 ? 1 : 0) + (ragged ? 2 : 0);
-  void (*const fns[4])(mla::SplitArgs) = {mla::mla_split_kernel<false, false>, mla::mla_split_kernel<true, false>,
-                                          mla::mla_split_kernel<false, true>, mla::mla_split_kernel<true, true>};
-  static bool attr_set[4] = {false, false, false, false};
+  const int v = kv_mode + (ragged ? 4 : 0);
+  void (*const fns[8])(mla::SplitArgs) = {
+      mla::mla_split_kernel<0, false>, mla::mla_split_kernel<1, false>, mla::mla_split_kernel<2, false>,
+      mla::mla_split_kernel<3, false>, mla::mla_split_kernel<0, true>,  mla::mla_split_kernel<1, true>,
+      mla::mla_split_kernel<2, true>,  mla::mla_split_kernel<3, true>};
+  static bool attr_set[8] = {false, false, false, false, false, false, false, false};
   if (!attr_set[v]) {
     // dynamic LDS above 64 KB: raise the per-kernel limit once to what the
     // kernel uses (static and dynamic LDS together stay within the 160 KB a

@@ -31,15 +31,15 @@ def test_exports_every_declared_function(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert mla.mla_abi_version() == 2
+    assert mla.mla_abi_version() == 3
     for code, name in [(0, "MLA_OK"), (1, "MLA_ERR_INVALID_VALUE"), (2, "MLA_ERR_NOT_SUPPORTED"),
                        (3, "MLA_ERR_WORKSPACE_TOO_SMALL"), (4, "MLA_ERR_HIP"), (99, "MLA_ERR_UNKNOWN")]:
         assert mla.status_name(code) == name
 
 
 def test_params_struct_layout():
-    # 10 int32, 2 float, 3 int32, no padding
-    assert ctypes.sizeof(mla.mla_decode_params) == 15 * 4
+    # 10 int32, 2 float, 4 int32, no padding
+    assert ctypes.sizeof(mla.mla_decode_params) == 16 * 4
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -68,6 +68,9 @@ def test_params_struct_layout():
     (dict(num_splits=1025), mla.MLA_ERR_INVALID_VALUE),
     (dict(min_work_units=-3), mla.MLA_ERR_INVALID_VALUE),
     (dict(num_cus=-1), mla.MLA_ERR_INVALID_VALUE),
+    (dict(quantize_q_fp8=1), mla.MLA_ERR_INVALID_VALUE),                             # bf16 pool
+    (dict(kv_dtype=mla.MLA_KV_FP8_E4M3FN, quantize_q_fp8=2), mla.MLA_ERR_INVALID_VALUE),
+    (dict(kv_dtype=mla.MLA_KV_FP8_E4M3FN, quantize_q_fp8=-1), mla.MLA_ERR_INVALID_VALUE),
 ])
 def test_invalid_params_rejected(L, kw, status):
     p = good(**kw)
