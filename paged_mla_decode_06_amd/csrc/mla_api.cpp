@@ -58,12 +58,9 @@ mla_status device_info(DeviceInfo* out) {
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.f; }
 
 // How the split kernel takes the pool's elements (the kKv* modes of the kernels).
-#ifndef MLA_F8_EXACT_MODE
-#define MLA_F8_EXACT_MODE 1
-#endif
 int kv_mode(const mla_decode_params* p) {
   if (p->kv_dtype != MLA_KV_FP8_E4M3FN) return 0;
-  return p->quantize_q_fp8 ? 2 : MLA_F8_EXACT_MODE;
+  return p->quantize_q_fp8 ? 2 : 1;
 }
 
 // Checks that need no device.  Returns MLA_OK or the error.

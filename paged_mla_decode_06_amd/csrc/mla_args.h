@@ -74,9 +74,8 @@ struct AppendArgs {
 }  // namespace mla
 
 extern "C" {
-// kv_mode: 0 bf16 pool; 1 fp8 pool converted by the loaders; 2 fp8 pool with
-// the query quantised and fp8 products; 3 fp8 pool converted at the fragment
-// reads.
+// kv_mode: 0 bf16 pool; 1 fp8 pool, codes converted to bf16 at the fragment
+// reads; 2 fp8 pool with the query quantised and fp8 score products.
 hipError_t mla_launch_split(const mla::SplitArgs* a, int kv_mode, hipStream_t stream);
 hipError_t mla_launch_combine(const mla::CombineArgs* a, hipStream_t stream);
 hipError_t mla_launch_gather(const void* pool, const int32_t* bt, const int32_t* seq_lens, int32_t W, int32_t P,

@@ -63,9 +63,6 @@ constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
 #ifndef MLA_F8_SC
 #define MLA_F8_SC 2
 #endif
-#ifndef MLA_F8_DEFER
-#define MLA_F8_DEFER 1
-#endif
 constexpr int kRowsPerWave = 16 * kRowBlocksPerWave;
 static_assert(kRowBlocksPerWave == 1, "one 16-row MFMA block per wave");
 // A split workgroup runs three kinds of wave in a pipeline over the KV tiles
@@ -94,7 +91,6 @@ constexpr int kLoaderWaves = 4;
 constexpr int kSplitWaves = kRowGroups + kPVWaves + kLoaderWaves;
 static_assert(kSplitWaves % 4 == 0 && kSplitWaves <= 16, "whole waves per SIMD, at most 1024 threads");
 constexpr int kSplitThreads = 64 * kSplitWaves;
-constexpr int kLoaderThreads = 64 * kLoaderWaves;
 constexpr int kRowBytes = kRowDim * 2;             // 1152: one bf16 row in LDS
 constexpr int kTileBytes = kTile * kRowBytes;      // 36864
 constexpr int kChunks = kTile * kRowDim * 2 / 16;  // 2304 16-byte chunks per bf16 tile
@@ -109,17 +105,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
 // How the pool's elements reach the matrix unit (the KV template parameter
 // of the split kernel):
-//   kKvBf16     bf16 pool: bf16 tiles in LDS, bf16 products.
-//   kKvFp8Cvt   e4m3fn pool: the loader waves convert the codes to bf16 on
-//               their way into LDS (exactly), bf16 products.
-//   kKvFp8Tile  e4m3fn pool: the codes are staged in LDS as they are, and K
-//               and V^T are converted to bf16 (exactly) as their MFMA
-//               fragments are read; bf16 products.
-//   kKvFp8Q     e4m3fn pool, codes staged as they are; the query rows are
-//               quantised to e4m3fn and the scores are fp8 products; V^T is
-//               converted to bf16 at its fragment read.
-constexpr int kKvBf16 = 0, kKvFp8Cvt = 1, kKvFp8Q = 2, kKvFp8Tile = 3;
-constexpr bool fp8_tile(int kv) { return kv == kKvFp8Q || kv == kKvFp8Tile; }
+//   kKvBf16  bf16 pool: bf16 tiles in LDS, bf16 products.
+//   kKvFp8   e4m3fn pool: the codes are staged in LDS as they are, and K and
+//            V^T are converted to bf16 (exactly) as their MFMA fragments are
+//            read; bf16 products.
+//   kKvFp8Q  e4m3fn pool, codes staged as they are; the query rows are
+//            quantised to e4m3fn and the scores are fp8 products; V^T is
+//            converted to bf16 at its fragment read.
+constexpr int kKvBf16 = 0, kKvFp8 = 1, kKvFp8Q = 2;
+constexpr bool fp8_tile(int kv) { return kv != kKvBf16; }
 
 static_assert(kChunks % 64 == 0, "tile must be a whole number of wave-wide loads");
 static_assert(kTileLoads % kLoaderWaves == 0, "every loader wave issues the same number of tile loads");
@@ -292,16 +286,16 @@ struct PageWindow {
 // page (tiles are 32-token aligned and the page size is 32 or 64), so a tile
 // is one contiguous run of global memory.
 //
-// bf16 pool: each wave issues wave-wide 16-byte loads that write LDS directly
+// Loader waves issue wave-wide 16-byte loads that write LDS directly
 // (global_load_lds_dwordx4: lane l lands at the wave's LDS base + 16*l); a
 // lane picks the global chunk whose swizzled LDS position is its own.  Lanes
-// of rows past the piece's last token issue no load: those LDS rows keep
-// zeros or an earlier tile's (finite) rows, and their scores are masked.
+// of rows past the piece's last token re-read a chunk of the tile's first
+// row, so every LDS row holds finite values; their scores are masked.
 template <int KV>
 struct Stage;
 
 template <>
-struct Stage<0> {
+struct Stage<kKvBf16> {
   // Load i of loader wave w fills the 64 physical LDS chunks starting at
   // P = 64*(w + kLoaderWaves*i).  The chunk p = P + l of lane l holds logical
   // chunk (p mod 72) ^ z(r) of row r = p / 72, z(r) = swz(r), so its
@@ -355,7 +349,7 @@ struct Stage<0> {
     const uint32_t dst = (uint32_t)(uintptr_t)(buf + wave * 1024);
     // Opaque copies: the offsets are unpacked here, once per tile, instead of
     // being hoisted out of the tile loop as nine live registers.
-    Stage<0> o = *this;
+    Stage<kKvBf16> o = *this;
 #pragma unroll
     for (int j = 0; j < kPacked; j++) asm("" : "+v"(o.xoff[j]));
     if (ts + kTile <= tok_end) {
@@ -385,105 +379,16 @@ struct Stage<0> {
   }
 };
 
-#ifndef MLA_F8_CVT_DIRECT
-#define MLA_F8_CVT_DIRECT 1
-#endif
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
-#if MLA_F8_CVT_DIRECT
   // Two e4m3fn codes (the low or the high half of the word) straight to a
   // bf16 pair by the gfx950 scaled conversion with scale 1: every e4m3fn
   // value is a bf16 value, so the conversion is exact.
   typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, (bf16x2_cvt_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, HI));
-#else
-  // e4m3fn -> fp32 is exact; every e4m3fn value is a bf16 value, so keeping
-  // the upper 16 bits of each fp32 is exact too.  The pair is taken as one
-  // 64-bit value and packed with a byte permute: extracting the second float
-  // of the intrinsic's result element-wise was compiled to a copy of the
-  // first one.
-  const u32x2_t f = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_cvt_pk_f32_fp8((int)word, HI));
-  return __builtin_amdgcn_perm(f[1], f[0], 0x07060302u);
-#endif
 }
 
-// fp8 pool: global -> registers, 16 codes (a 16-byte chunk, one of a row's 36)
-// per load, converted once per tile and stored to LDS as bf16: the two
-// 16-byte LDS chunks 2c and 2c+1 of the row.  A tile's 1152 chunks take
-// 4.5 loads per loader lane: the fifth only in loader waves 0 and 1.  The
-// rows of a tile are consecutive slots of one page, so chunk m of row r is
-// at byte 576*r + 16*m of the tile's first row.
-template <>
-struct Stage<1> {
-  static constexpr int kChunks = kTile * kRowDim / 16;   // 1152
-  static constexpr int kRowChunks = kRowDim / 16;        // 36
-  static constexpr int kPer = (kChunks + kLoaderThreads - 1) / kLoaderThreads;   // 5
-  static_assert(kChunks % 64 == 0, "every loader wave loads whole or no chunks");
-  static_assert(kTile == 32 && kRowChunks == 36, "chunk_of assumes 16 row pairs of 36 chunks");
-  u32x4_t v[kPer];
-  __device__ __forceinline__ void init(int) {}
-  // The tile chunk (row r, chunk m of the row's 36) that slot q = lt + 256*i
-  // of the loader threads carries.  Each chunk becomes the two 16-byte LDS
-  // chunks 2m and 2m + 1 of row r.  The LDS takes a 16-byte write eight
-  // lanes at a time over 128 bytes of banks (measured: the bank-conflict
-  // counter of this kernel matches that model, and no other, across three
-  // store orders), so the eight chunks a group of eight lanes writes must be
-  // distinct modulo eight.  Eight lanes on consecutive chunks of one row
-  // write chunks 32 bytes apart, two to a bank.  Instead lanes 0..3 of a
-  // group take chunks 4a .. 4a+3 of row 2s and lanes 4..7 the same chunks of
-  // row 2s + 1 (group G = 9s + a, nine groups per row pair): the even row's
-  // chunks land on the even 16-byte bank slots and the odd row's on the odd
-  // ones (an odd row's swizzle flips bit 0; the 1152-byte row pitch is a
-  // whole number of bank periods), so both writes are free of conflicts.
-  __device__ __forceinline__ static void chunk_of(int q, int& r, int& m) {
-    const int G = q >> 3, k = q & 7;
-    const int s = (G * 57) >> 9;   // G / 9 for G < 144
-    r = 2 * s + (k >> 2);
-    m = 4 * (G - 9 * s) + (k & 3);
-  }
-  // Called by the loader waves; lt = thread index among them.
-  __device__ __forceinline__ void load(const SplitArgs& a, PageWindow& pw, int b, int ts, int tok_end) {
-    const int lt = threadIdx.x - 64 * kLoaderWave0;
-    const char* base = nullptr;
-    if (ts < tok_end) {
-      const int32_t page = pw.page(a, b, ts >> a.p_shift);
-      if ((uint32_t)page < (uint32_t)a.N)
-        base = (const char*)a.pool + (((int64_t)page << a.p_shift) + (ts & (a.P - 1))) * kRowDim;
-    }
-#pragma unroll
-    for (int i = 0; i < kPer; i++) {
-      const int q = lt + kLoaderThreads * i;
-      int r, m;
-      chunk_of(q, r, m);
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (base != nullptr && q < kChunks && ts + r < tok_end) x = *(const u32x4_t*)(base + r * kRowDim + 16 * m);
-      v[i] = x;
-    }
-  }
-  __device__ __forceinline__ void store(lds_char* buf) const {
-    const int lt = threadIdx.x - 64 * kLoaderWave0;
-#pragma unroll
-    for (int i = 0; i < kPer; i++) {
-      const int q = lt + kLoaderThreads * i;
-      if (q >= kChunks) continue;
-      int r, m;
-      chunk_of(q, r, m);
-      u32x4_t y0, y1;
-      y0[0] = fp8x2_to_bf16x2<false>(v[i][0]);
-      y0[1] = fp8x2_to_bf16x2<true>(v[i][0]);
-      y0[2] = fp8x2_to_bf16x2<false>(v[i][1]);
-      y0[3] = fp8x2_to_bf16x2<true>(v[i][1]);
-      y1[0] = fp8x2_to_bf16x2<false>(v[i][2]);
-      y1[1] = fp8x2_to_bf16x2<true>(v[i][2]);
-      y1[2] = fp8x2_to_bf16x2<false>(v[i][3]);
-      y1[3] = fp8x2_to_bf16x2<true>(v[i][3]);
-      *(__attribute__((address_space(3))) u32x4_t*)(buf + lds_off(r, 2 * m)) = y0;
-      *(__attribute__((address_space(3))) u32x4_t*)(buf + lds_off(r, 2 * m + 1)) = y1;
-    }
-  }
-};
-
-// fp8 pool, codes staged as they are (kKvFp8Tile, kKvFp8Q): a tile is 32
+// fp8 pool: the codes are staged as they are.  A tile is 32
 // rows of 576 bytes (36 16-byte chunks) in the first half of its ring buffer.
 // Logical chunk c of row r sits at physical chunk c ^ swz8(r): only the low
 // two bits change, so a chunk stays inside its aligned group of four (36 is
@@ -570,7 +475,7 @@ struct Stage8 {
   }
 };
 template <>
-struct Stage<kKvFp8Tile> : Stage8 {};
+struct Stage<kKvFp8> : Stage8 {};
 template <>
 struct Stage<kKvFp8Q> : Stage8 {};
 
@@ -708,7 +613,7 @@ struct LaneOffsetsSel {
   typedef LaneOffsets type;
 };
 template <>
-struct LaneOffsetsSel<kKvFp8Tile> {
+struct LaneOffsetsSel<kKvFp8> {
   typedef LaneOffsets8 type;
 };
 template <>
@@ -830,10 +735,13 @@ __device__ __forceinline__ u32x2_t bf16x8_to_e4m3(u32x4_t v) {
 __device__ __forceinline__ void qk_tile_q8(const QCodes& q8, lds_cchar* cur, const LaneOffsets8& lo_, f32x4v_t& s0,
                                            f32x4v_t& s1) {
   typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
-  lds_cchar* kp[2][2] = {{opaque_lds(cur + lo_.kbase[0][0]), opaque_lds(cur + lo_.kbase[0][1])},
-                         {opaque_lds(cur + lo_.kbase[1][0]), opaque_lds(cur + lo_.kbase[1][1])}};
+  lds_cchar* kp[2][2] = {{cur + lo_.kbase[0][0], cur + lo_.kbase[0][1]}, {cur + lo_.kbase[1][0], cur + lo_.kbase[1][1]}};
+  // Each read's address is opaque: left alone, the compiler pairs the reads
+  // 64 bytes apart into one two-address read, which the LDS serves with bank
+  // conflicts (measured: 19.5 M conflict cycles per fp8 dispatch instead of
+  // 0.5 M).
   auto kread = [&](int tb, int k) -> u32x2_t {
-    return *(__attribute__((address_space(3))) const u32x2_t*)(kp[tb][k & 1] + 64 * (k >> 1));
+    return *(__attribute__((address_space(3))) const u32x2_t*)opaque_lds(kp[tb][k & 1] + 64 * (k >> 1));
   };
   // MFMAs i = 0..7: 16x16x128 step kb = i/2 of block tb = i%2; i = 8..11:
   // 16x16x32 rope step s = (i-8)/2 of block tb = i%2
@@ -1042,47 +950,15 @@ __device__ void load_piece(const SplitArgs& a, lds_char* lds, Stage<KV>& stg, co
   const int nt = pc.tile1 - pc.tile0;
   PageWindow pw;
   pw.init(a, b, (pc.tile0 * kTile) >> a.p_shift, (tok_end + a.P - 1) >> a.p_shift);
-  if constexpr (KV == kKvFp8Cvt) {
-#if MLA_F8_DEFER
-    // fp8 codes go through registers: tile t's codes are loaded in interval
-    // t-3 and converted into LDS in interval t-2 (its buffer is free from
-    // then on), so each tile's HBM latency overlaps a whole interval instead
-    // of stalling the loader wave in the interval that issues it.
-    auto load = [&](int t) { stg.load(a, pw, b, (pc.tile0 + t) * kTile, tok_end); };
-    auto store = [&](int t) { stg.store(lds + tile_buf(t) * kTileBytes); };   // waits for tile t's loads
-    if (nt > 0) {
-      load(0);
-      store(0);
-    }
-    if (nt > 1) load(1);
-    for (int j = -1; j < nt; j++) {
-      // tile j+1 is in LDS before barrier j
-      lds_barrier();
-      if (j + 2 < nt) store(j + 2);
-      if (j + 3 < nt) load(j + 3);
-    }
-#else
-    auto put = [&](int t) {
-      stg.load(a, pw, b, (pc.tile0 + t) * kTile, tok_end);
-      stg.store(lds + tile_buf(t) * kTileBytes);   // waits for its own loads
-    };
-    for (int t = 0; t < 2 && t < nt; t++) put(t);
-    for (int j = -1; j < nt; j++) {
-      lds_barrier();
-      if (j + 3 < nt) put(j + 3);
-    }
-#endif
-  } else {
-    auto put = [&](int t) {   // tile t of the piece into its ring buffer
-      stg.issue(a, lds + tile_buf(t) * kTileBytes, pw, b, (pc.tile0 + t) * kTile, tok_end, lw);
-    };
-    for (int t = 0; t < 2 && t < nt; t++) put(t);
-    for (int j = -1; j < nt; j++) {
-      // tile j+1 is in LDS before barrier j; tile j+2 may still be in flight
-      stg.wait(j + 2 < nt ? 1 : 0);
-      lds_barrier();
-      if (j + 3 < nt) put(j + 3);
-    }
+  auto put = [&](int t) {   // tile t of the piece into its ring buffer
+    stg.issue(a, lds + tile_buf(t) * kTileBytes, pw, b, (pc.tile0 + t) * kTile, tok_end, lw);
+  };
+  for (int t = 0; t < 2 && t < nt; t++) put(t);
+  for (int j = -1; j < nt; j++) {
+    // tile j+1 is in LDS before barrier j; tile j+2 may still be in flight
+    stg.wait(j + 2 < nt ? 1 : 0);
+    lds_barrier();
+    if (j + 3 < nt) put(j + 3);
   }
   lds_barrier();
   lds_barrier();
@@ -1159,10 +1035,8 @@ __device__ void qk_piece(const SplitArgs& a, lds_char* lds, const LaneOffsetsOf<
       lds_cchar* cur = lds + tile_buf(t) * kTileBytes;
       if constexpr (KV == kKvFp8Q)
         qk_tile_q8(q8, cur, lo_, s0, s1);
-      else if constexpr (KV == kKvFp8Tile)
+      else if constexpr (KV == kKvFp8)
         qk_tile_cvt<MLA_F8_KA, MLA_F8_SC>(qf, cur, lo_, s0, s1);
-      else if constexpr (KV == kKvFp8Cvt)
-        qk_tile<MLA_F8_KA, MLA_F8_SC>(qf, cur, lo_, s0, s1);
       else
         qk_tile<MLA_KA, MLA_SC>(qf, cur, lo_, s0, s1);
       softmax_tile<fp8_tile(KV)>(s0, s1, m_run, l_run, (pc.tile0 + t) * kTile, limit, lim_min, a.scale_log2,
@@ -1203,8 +1077,6 @@ __device__ void pv_piece(const SplitArgs& a, lds_char* lds, const LaneOffsetsOf<
       lds_cchar* ain = lds + kABufOff + (j & 1) * (kRowsPerBlock * 4) + 16 * i16 + 4 * rg0;
       if constexpr (fp8_tile(KV))
         pv_tile8<MLA_F8_VA>(acc, vcur, lo_, pin, ain);
-      else if constexpr (KV == kKvFp8Cvt)
-        pv_tile<MLA_F8_VA>(acc, vcur, lo_, pin, ain);
       else
         pv_tile<MLA_VA>(acc, vcur, lo_, pin, ain);
     }
@@ -1867,15 +1739,14 @@ size_t mla_split_lds_bytes(int32_t B, int32_t num_splits) {
 }
 
 hipError_t mla_launch_split(const mla::SplitArgs* a, int kv_mode, hipStream_t stream) {
-  if (kv_mode < 0 || kv_mode > 3) return hipErrorInvalidValue;
+  if (kv_mode < 0 || kv_mode > 2) return hipErrorInvalidValue;
   const size_t lds = mla_split_lds_bytes(a->B, a->num_splits);
   const bool ragged = a->qo_indptr != nullptr;
-  const int v = kv_mode + (ragged ? 4 : 0);
-  void (*const fns[8])(mla::SplitArgs) = {
-      mla::mla_split_kernel<0, false>, mla::mla_split_kernel<1, false>, mla::mla_split_kernel<2, false>,
-      mla::mla_split_kernel<3, false>, mla::mla_split_kernel<0, true>,  mla::mla_split_kernel<1, true>,
-      mla::mla_split_kernel<2, true>,  mla::mla_split_kernel<3, true>};
-  static bool attr_set[8] = {false, false, false, false, false, false, false, false};
+  const int v = kv_mode + (ragged ? 3 : 0);
+  void (*const fns[6])(mla::SplitArgs) = {mla::mla_split_kernel<0, false>, mla::mla_split_kernel<1, false>,
+                                          mla::mla_split_kernel<2, false>, mla::mla_split_kernel<0, true>,
+                                          mla::mla_split_kernel<1, true>,  mla::mla_split_kernel<2, true>};
+  static bool attr_set[6] = {false, false, false, false, false, false};
   if (!attr_set[v]) {
     // dynamic LDS above 64 KB: raise the per-kernel limit once to what the
     // kernel uses (static and dynamic LDS together stay within the 160 KB a
