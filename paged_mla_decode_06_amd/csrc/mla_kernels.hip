@@ -39,12 +39,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;                      // combine / gather / plan kernels
-// Split kernel shape: kSplitWaves waves of kRowBlocksPerWave 16-row MFMA blocks
-// each; kSplitWaves * kRowBlocksPerWave * 16 == kRowsPerBlock.
-#ifndef MLA_ROWBLOCKS_PER_WAVE
-#define MLA_ROWBLOCKS_PER_WAVE 1
-#endif
-constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
+// Read-ahead depths and accumulation chains of the tile loops (bf16 and fp8
+// tiles): K reads ahead of their MFMAs, Vt reads ahead, score chains.
 #ifndef MLA_KA
 #define MLA_KA 3
 #endif
@@ -63,8 +59,7 @@ constexpr int kRowBlocksPerWave = MLA_ROWBLOCKS_PER_WAVE;
 #ifndef MLA_F8_SC
 #define MLA_F8_SC 2
 #endif
-constexpr int kRowsPerWave = 16 * kRowBlocksPerWave;
-static_assert(kRowBlocksPerWave == 1, "one 16-row MFMA block per wave");
+constexpr int kRowsPerWave = 16;   // one 16-row MFMA block per QK wave
 // A split workgroup runs three kinds of wave in a pipeline over the KV tiles
 // of a piece (waves are spread evenly over the four SIMDs: one QK wave, two
 // PV waves and one loader wave on each, 128 registers per wave):
