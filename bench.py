@@ -208,7 +208,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; the decode runs on one GPU "
-              f"(requests shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+              f"(across GPUs the requests would shard with no exchange between them)", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_calibration:
