@@ -16,10 +16,12 @@
 //   P^T = exp2(S^T*scale*log2e - m)  (online softmax, lazily rescaled)
 //   O^T[512 x 16 rows]    += V^T[512 x 32 tok] . P^T[32 x 16]  (32 MFMA 16x16x32 bf16)
 // With K as the A operand and Q^T as B, the S^T accumulator leaves each lane
-// holding 8 tokens of its own row, which is exactly the B-operand layout P^T
-// needs for the second product, so P never leaves registers and the row max
+// holding 8 tokens of its own row, which is exactly the lane's B-operand
+// layout of P^T in the second product: the QK wave stores P as that 16-byte
+// operand in LDS and a P.V wave reads it back unchanged, and the row max
 // needs two lane exchanges.  V^T comes from the same LDS tile through the
-// gfx950 transposing LDS read (ds_read_b64_tr_b16).
+// gfx950 transposing LDS read (ds_read_b64_tr_b16; fp8 tiles: ds_read_b64_tr_b8
+// and an exact conversion of the codes to bf16).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -112,7 +114,8 @@ constexpr bool fp8_tile(int kv) { return kv != kKvBf16; }
 
 static_assert(kChunks % 64 == 0, "tile must be a whole number of wave-wide loads");
 static_assert(kTileLoads % kLoaderWaves == 0, "every loader wave issues the same number of tile loads");
-// KV tile buffers in LDS: kTileBufs - 1 tiles are in flight while one is consumed.
+// KV tile buffers in LDS: in each interval the P.V waves read one tile, the QK
+// waves the next, and the two after those are in flight.
 constexpr int kTileBufs = 4;
 // LDS of a split workgroup: the tile ring; two sets (by tile parity) of the
 // softmax weights P (one 1 KB block per row group: its lanes' MFMA operands)
@@ -171,10 +174,9 @@ __device__ __forceinline__ QExtent q_extent(const Args& a, int32_t b) {
 // two of the rope part at 0 and 64 from pr.  One asm statement also waits
 // for them: nothing the compiler emits can touch the registers before the
 // data is there, and the compiler keeps no record of these loads, so it
-// never waits for them (and for every tile load behind them) inside the tile
-// loop.  The wait covers every vector memory operation issued before, which
-// is why the first tiles' loads are issued before this: their latency then
-// overlaps the query's.
+// never waits for them inside the tile loop.  The wait covers every vector
+// memory operation the wave issued before; the QK waves that call this issue
+// no tile loads (the loader waves do), so it waits for the query alone.
 #define MLA_Q_OUT(k) "=&v"(q[k])
 __device__ __forceinline__ void load_q_fragments(u32x4_t (&q)[18], const void* pn, const void* pr) {
   asm volatile(
