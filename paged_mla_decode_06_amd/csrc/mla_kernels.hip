@@ -1465,13 +1465,17 @@ struct CombineShape {
 // a full-size decode (up to 2048 workgroups) runs in one round.  One row per
 // workgroup: fewer, wider workgroups, up to 128 VGPRs.
 //
-// kByGroup (balanced plans with fewer groups than requests, B <= kByGroupMaxB):
-// the grid covers groups instead of requests, NG * nrb * 16 workgroups.  A
+// kByGroup (balanced plans with B <= kByGroupMaxB, when the groups are fewer
+// than the requests or the batch is ragged): the grid covers the split
+// kernel's workgroups instead of the requests, NG * nrb * 16 workgroups.  A
 // split request's last tile lies in the share of exactly one group g1, and
 // that share starts inside the request (its first tile lies in an earlier
 // group), so the request holding position start(g) is the only one the
 // workgroups of group g may have to merge: they merge it when it is split
-// and ends in g's share.  Unsplit requests then cost no workgroup.
+// and ends in g's share.  Unsplit requests, and row blocks a short request
+// of a ragged batch does not have, then cost no workgroup.  Under a
+// row-block class plan the same holds on each class's own line of positions
+// and groups.
 constexpr int kByGroupMaxB = 4 * kThreads;   // offsets found with one load round per thread
 template <int kWaves, bool kByGroup>
 __global__ __launch_bounds__(kThreads, kWaves == 1 ? 8 : 4) void mla_combine_kernel(CombineArgs a) {
@@ -1488,26 +1492,57 @@ __global__ __launch_bounds__(kThreads, kWaves == 1 ? 8 : 4) void mla_combine_ker
   int64_t NGc = a.NG, slot_base = 0;   // the plan's groups (of the request's class) and its first slot
   int32_t nrbc = a.nrb;                // workgroups per group
   if constexpr (kByGroup) {
-    // every wave of the workgroup takes part before any returns
-    const int64_t g = blk / a.nrb;
-    rb = (int32_t)(blk - g * a.nrb);
-    total = a.pos_off_ws[a.B];
-    const int64_t v = wg_start(g, total, a.NG);
+    // blk is a split workgroup's number: g * nrb + rb in the uniform plan, or
+    // the dense number of a workgroup of the row-block class plan (class n's
+    // groups take numbers base_n .. base_n + G_n * n - 1, n per group).
+    // Every wave of the workgroup takes part before any returns.
+    int64_t g = 0;
+    int32_t n = 0;   // class of a class plan's group; 0: the uniform plan
+    if (a.class_tab != nullptr && a.class_tab[0] == 1) {
+#pragma unroll
+      for (int k = 1; k <= kMaxClasses; k++) {
+        const int64_t base = a.class_tab[kTabBase + k], Gk = a.class_tab[kTabG + k];
+        if (blk >= base && blk < base + Gk * k) {
+          n = k;
+          g = (blk - base) / k;
+          rb = (int32_t)(blk - base - g * k);
+          total = a.class_tab[kTabT + k];
+          NGc = Gk;
+          nrbc = k;
+          slot_base = 2 * base;
+        }
+      }
+      if (n == 0) return;   // a slot the class plan leaves empty
+    } else {
+      g = blk / a.nrb;
+      rb = (int32_t)(blk - g * a.nrb);
+      total = a.pos_off_ws[a.B];
+    }
+    const int64_t v = wg_start(g, total, NGc);
     __shared__ int32_t found;
     if (threadIdx.x == 0) found = -1;
     __syncthreads();
+    // the request holding position v on the group's line: one request does
+    // (on a class's line, only that class's requests take positions)
 #pragma unroll
     for (int k = 0; k < kByGroupMaxB / kThreads; k++) {
       const int bb = (int)threadIdx.x + kThreads * k;
-      if (bb < a.B && a.pos_off_ws[bb] <= v && v < a.pos_off_ws[bb + 1]) found = bb;   // one request holds v
+      if (bb >= a.B) continue;
+      const int64_t o = a.pos_off_ws[bb];
+      if (n == 0) {
+        if (o <= v && v < a.pos_off_ws[bb + 1]) found = bb;
+      } else if (row_blocks(q_extent<true>(a, bb).qb, a.H) == n) {
+        if (o <= v && v < o + positions_of(clamp_len(a.seq_lens[bb], a.max_seq_len))) found = bb;
+      }
     }
     __syncthreads();
     b = found;
     if (b < 0) return;   // an empty share at the end
     first_pos = a.pos_off_ws[b];
-    const int32_t U = a.pos_off_ws[b + 1] - (int32_t)first_pos - kPieceCost;
-    g0 = first_group(first_pos, total, a.NG);
-    g1 = last_group(first_pos, U, total, a.NG);
+    const int32_t U = n == 0 ? a.pos_off_ws[b + 1] - (int32_t)first_pos - kPieceCost
+                             : units_of(clamp_len(a.seq_lens[b], a.max_seq_len));
+    g0 = first_group(first_pos, total, NGc);
+    g1 = last_group(first_pos, U, total, NGc);
     if (g1 != g || g0 == g1) return;   // not a split request that ends in this share
   } else {
     b = (int32_t)(blk / a.nrb);
@@ -1761,10 +1796,11 @@ hipError_t mla_launch_split(const mla::SplitArgs* a, int kv_mode, hipStream_t st
 hipError_t mla_launch_combine(const mla::CombineArgs* a, hipStream_t stream) {
   // a workgroup per row when requests are split into many pieces on average
   const bool wide = a->num_splits > 0 ? a->num_splits >= 8 : a->NG >= 4 * (int64_t)a->B;
-  // the grid over groups when they are fewer than the requests
-  // (not with a class plan, whose groups are per class)
-  const bool by_group = !wide && a->num_splits == 0 && a->NG < a->B && a->B <= mla::kByGroupMaxB &&
-                        a->class_tab == nullptr;
+  // the grid over the split workgroups when the groups are fewer than the
+  // requests, or when the split kernel may plan in row-block classes (its
+  // workgroups then take at most NG * nrb dense numbers)
+  const bool by_group = !wide && a->num_splits == 0 && a->B <= mla::kByGroupMaxB &&
+                        (a->NG < a->B || a->class_tab != nullptr);
   const int rows_per_wg = wide ? mla::CombineShape<4>::kRowsPerWg : mla::CombineShape<1>::kRowsPerWg;
   const int64_t units = by_group ? a->NG : (int64_t)a->B;
   const int64_t blocks = units * a->nrb * (mla::kRowsPerBlock / rows_per_wg);
