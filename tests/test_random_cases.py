@@ -3,7 +3,8 @@ query length, head count, page size, ragged lengths (empty requests
 included), pool type and k_scale, split mode -- drawn per seed, so that
 combinations the hand-picked cases miss are covered too.  The same draws
 drive ragged batches and the query read from two strided parts with the
-rotary embedding."""
+rotary embedding, and the fp8 pool with the query cast to e4m3fn; a
+medium-size family adds larger batches, head counts and lengths."""
 import dataclasses
 
 import numpy as np
@@ -22,6 +23,7 @@ import oracle_pins as P
 from mla_synth import ragged, rope_cache
 import gpu_util as G
 from test_ragged import run_ragged
+from test_q_fp8 import _oracle_q8, _run_q8
 
 
 def _draw(seed):
@@ -42,7 +44,7 @@ def _draw(seed):
     return inp, kw, r
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_decode(seed):
     inp, kw, _ = _draw(seed)
     o, l = G.run(inp, **kw)
@@ -51,7 +53,7 @@ def test_random_decode(seed):
                                                   f"P={inp.page_size} fp8={inp.kv_fp8} {kw}")
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_ragged(seed):
     inp, kw, r = _draw(100 + seed)
     q_lens = r.integers(0, inp.q_len + 1, size=inp.batch)
@@ -76,7 +78,7 @@ def _padded_view(t, head_major, pad_w, extra, dev="cuda"):
     return v
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_query_parts(seed):
     """The query as two strided parts (random padding, token- or head-major)
     with or without the rotary embedding (either pairing), at random
@@ -116,3 +118,57 @@ def test_random_query_parts(seed):
     assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32)), f"{what}: LSEs differ"
     ro, rl = oracle.default().decode(inp_r)
     G.compare(out1.float().cpu().numpy(), lse1.cpu().numpy(), ro, rl, fp8=inp.kv_fp8, what=what)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_query_fp8(seed):
+    """The fp8 pool with the query cast to e4m3fn, on the random draws that
+    hold an fp8 pool, against the oracle's decode of the cast query."""
+    inp, kw, _ = _draw(900 + seed)
+    if not inp.kv_fp8:
+        pytest.skip("this draw holds a bf16 pool")
+    o, l = _run_q8(inp, **kw)
+    ro, rl = _oracle_q8(inp)
+    G.compare(o, l, ro, rl, fp8=True, what=f"fp8 query seed {seed}: B={inp.batch} q={inp.q_len} H={inp.heads} {kw}")
+
+
+def _draw_medium(seed):
+    """Larger draws: up to 64 requests of 64 or 128 heads, up to 3000 tokens,
+    so that split rows, the combine's grids and (ragged) row-block classes
+    all occur."""
+    r = np.random.default_rng(9100 + seed)
+    B = int(r.integers(1, 65))
+    q_len = int(r.integers(1, 5))
+    H = int(r.choice([64, 128]))
+    Pg = int(r.choice([32, 64]))
+    lens = r.integers(0, 3000, size=B)
+    lens[r.random(B) < 0.1] = 0
+    kv = "fp8" if r.random() < 0.4 else "bf16"
+    k_scale = float(r.choice([0.5, 1.5])) if kv == "fp8" else None
+    mode = r.choice(["auto", "auto", "forced", "units"])
+    kw = {"auto": {}, "forced": {"num_splits": int(r.integers(1, 12))},
+          "units": {"min_work_units": int(r.choice([r.integers(1, 64), r.integers(256, 1500)]))}}[mode]
+    inp = P.small(kv=kv, q_len=q_len, heads=H, page_size=Pg, lens=tuple(int(x) for x in lens), seed=9100 + seed,
+                  k_scale=k_scale)
+    return inp, kw, r
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_medium(seed):
+    """Medium-size draws, in turn a uniform batch, a ragged one (random query
+    lengths) and, for an fp8 pool, the query cast to e4m3fn."""
+    inp, kw, r = _draw_medium(seed)
+    kind = seed % 3
+    what = f"medium seed {seed} kind {kind}: B={inp.batch} q={inp.q_len} H={inp.heads} P={inp.page_size} " \
+           f"fp8={inp.kv_fp8} {kw}"
+    if kind == 1:
+        rg = ragged(inp, q_lens=r.integers(0, inp.q_len + 1, size=inp.batch))
+        o, l = run_ragged(rg, **kw)
+        ro, rl = RG.decode(oracle.default(), rg)
+    elif kind == 2 and inp.kv_fp8:
+        o, l = _run_q8(inp, **kw)
+        ro, rl = _oracle_q8(inp)
+    else:
+        o, l = G.run(inp, **kw)
+        ro, rl = oracle.default().decode(inp)
+    G.compare(o, l, ro, rl, fp8=inp.kv_fp8, what=what)
