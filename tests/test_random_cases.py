@@ -120,13 +120,21 @@ def test_random_query_parts(seed):
     G.compare(out1.float().cpu().numpy(), lse1.cpu().numpy(), ro, rl, fp8=inp.kv_fp8, what=what)
 
 
+def _draw_fp8(seed):
+    """The first of the draws 900 + 64*seed onwards that holds an fp8 pool
+    (each does with probability 0.35, so one of 64 does but for ~1e-12)."""
+    for s in range(900 + 64 * seed, 964 + 64 * seed):
+        inp, kw, _ = _draw(s)
+        if inp.kv_fp8:
+            return inp, kw
+    raise AssertionError(f"no fp8 draw among 64 from seed {seed}")
+
+
 @pytest.mark.parametrize("seed", range(24))
 def test_random_query_fp8(seed):
-    """The fp8 pool with the query cast to e4m3fn, on the random draws that
-    hold an fp8 pool, against the oracle's decode of the cast query."""
-    inp, kw, _ = _draw(900 + seed)
-    if not inp.kv_fp8:
-        pytest.skip("this draw holds a bf16 pool")
+    """The fp8 pool with the query cast to e4m3fn on random draws, against the
+    oracle's decode of the cast query."""
+    inp, kw = _draw_fp8(seed)
     o, l = _run_q8(inp, **kw)
     ro, rl = _oracle_q8(inp)
     G.compare(o, l, ro, rl, fp8=True, what=f"fp8 query seed {seed}: B={inp.batch} q={inp.q_len} H={inp.heads} {kw}")
