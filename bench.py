@@ -262,17 +262,19 @@ def main():
     stream = torch.cuda.current_stream()
     ind = torch.from_numpy(rg.qo_indptr).to(dev) if rg is not None else None
 
-    # Every timed step records events on the stream both kernels run on: before
-    # the split kernel, after it, and after the combine.  The split kernel's
-    # duration is (start, split end) of its own step, the call's (start, call
-    # end), the GPU time of a whole step (start, next start).  A ragged call is
-    # bracketed as a whole (split kernel and combine).
+    # Every timed step records two events on the stream both kernels run on:
+    # before the split kernel and after it.  The split kernel's duration is
+    # (start, split end) of its own step; the GPU time of a whole call, combine
+    # and the gap to the next call included, is (start, next start).  A ragged
+    # call is bracketed as a whole (split kernel and combine).  A third event
+    # after the combine measured 3.3 us per step of its own on the DeepSeek
+    # workload, so the call is timed start to start instead.
     ev = HipEvents()
-    events = [(ev.create(), ev.create(), ev.create()) for _ in range(args.steps)]
+    events = [(ev.create(), ev.create()) for _ in range(args.steps)]
 
-    def step(i, e0, e1, e2):
+    def step(i, e0, e1):
         if rg is None:
-            mla.mla_decode_timed(p, qs[i % copies], pools[i % copies], bt, sl, out, lse, ws, stream, e0, e1, e2)
+            mla.mla_decode_timed(p, qs[i % copies], pools[i % copies], bt, sl, out, lse, ws, stream, e0, e1, None)
             return
         if e0 is not None:
             ev.record(e0, stream)
@@ -282,7 +284,7 @@ def main():
             ev.record(e1, stream)
 
     for i in range(args.warmup):
-        step(i, None, None, None)
+        step(i, None, None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -290,10 +292,12 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    split_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b, _ in events]))
-    call_ms = float(np.mean([ev.elapsed_ms(a, c) for a, _, c in events])) if rg is None else split_ms
+    split_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in events]))
     gpu_step_ms = float(np.mean([ev.elapsed_ms(events[k][0], events[k + 1][0])
                                  for k in range(args.steps - 1)])) if args.steps > 1 else float("nan")
+    # the whole call, split kernel to the next call's start (a single timed
+    # step has no next start: its split kernel alone then)
+    call_ms = gpu_step_ms if args.steps > 1 else split_ms
     for e in events:
         for x in e:
             ev.destroy(x)
@@ -345,10 +349,10 @@ def main():
                 "kernel": "mla_split_kernel" if rg is None else "mla_split_kernel + mla_combine_kernel (one call)",
                 "algorithmic_bytes_per_launch": split_bytes, "algorithmic_flops_per_launch": flops,
                 "hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
-                # the whole decode call (split kernel, combine and the gap
-                # between them): all its algorithmic bytes, output included,
-                # over the GPU time from before the split kernel to after the
-                # combine
+                # the whole decode call (split kernel, combine and the gaps
+                # around it): all its algorithmic bytes, output included, over
+                # the GPU time from before one call's split kernel to before
+                # the next call's
                 "call": {"kernels": "mla_split_kernel + mla_combine_kernel", "ms": round(call_ms, 5),
                          "algorithmic_bytes": nbytes,
                          "achieved": round(nbytes / (call_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
