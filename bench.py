@@ -262,15 +262,19 @@ def main():
     stream = torch.cuda.current_stream()
     ind = torch.from_numpy(rg.qo_indptr).to(dev) if rg is not None else None
 
-    # Every timed step records two events on the stream both kernels run on:
-    # before the split kernel and after it.  The split kernel's duration is
-    # (start, split end) of its own step; the GPU time of a whole call, combine
-    # and the gap to the next call included, is (start, next start).  A ragged
-    # call is bracketed as a whole (split kernel and combine).  A third event
-    # after the combine measured 3.3 us per step of its own on the DeepSeek
-    # workload, so the call is timed start to start instead.
+    # Every fourth timed step (every step when fewer than 8 are timed) records
+    # two events on the stream both kernels run on: before the split kernel
+    # and after it.  The split kernel's duration is (start, split end) of its
+    # own step; the GPU time of a whole call, combine and the gaps included,
+    # is (start, next sampled start) over the steps between them.  A ragged
+    # call is bracketed as a whole (split kernel and combine).  Event records
+    # take GPU time of their own (DeepSeek workload: 71.4 us a step with none,
+    # 73.6 with two on every step, 76.9 with a third after the combine), hence
+    # the sampling and no event after the combine.
     ev = HipEvents()
-    events = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    every = 4 if args.steps >= 8 else 1
+    sampled = list(range(0, args.steps, every))
+    events = {k: (ev.create(), ev.create()) for k in sampled}
 
     def step(i, e0, e1):
         if rg is None:
@@ -288,17 +292,17 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(args.warmup + k, *events[k])
+        step(args.warmup + k, *events.get(k, (None, None)))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    split_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in events]))
-    gpu_step_ms = float(np.mean([ev.elapsed_ms(events[k][0], events[k + 1][0])
-                                 for k in range(args.steps - 1)])) if args.steps > 1 else float("nan")
-    # the whole call, split kernel to the next call's start (a single timed
+    split_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in events.values()]))
+    spans = [(ev.elapsed_ms(events[a][0], events[b][0]), b - a) for a, b in zip(sampled, sampled[1:])]
+    gpu_step_ms = sum(t for t, _ in spans) / sum(n for _, n in spans) if spans else float("nan")
+    # the whole call, split kernel to the next call's start (a single sampled
     # step has no next start: its split kernel alone then)
-    call_ms = gpu_step_ms if args.steps > 1 else split_ms
-    for e in events:
+    call_ms = gpu_step_ms if spans else split_ms
+    for e in events.values():
         for x in e:
             ev.destroy(x)
     assert torch.isfinite(out.float()).all().item(), "non-finite output"
@@ -382,8 +386,12 @@ def main():
         "decode_tokens_per_s": round(q_rows / (ms_step * 1e-3), 1),
         "algorithmic_bytes": nbytes,
         "algorithmic_flops": flops,
-        "event_ms": {"split_kernel": round(split_ms, 5), "call": round(call_ms, 5), "gpu_step": round(gpu_step_ms, 5),
-                     "combine_and_launch_gaps": round(gpu_step_ms - split_ms, 5)},
+        # null where a figure does not exist: no GPU step from a single
+        # sampled step, and no separate combine time for a ragged call (its
+        # events bracket split kernel and combine together)
+        "event_ms": {"split_kernel": round(split_ms, 5), "call": round(call_ms, 5),
+                     "gpu_step": round(gpu_step_ms, 5) if spans else None,
+                     "combine_and_launch_gaps": round(gpu_step_ms - split_ms, 5) if spans and rg is None else None},
         "roofline": roofline,
         "path_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
         "kv_append": append_step,
